@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU. Together they are chosen so that a plausible
+mistake in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong rounding rule) fails at least one of them; test_oracle_mutations
+plants such mistakes and checks that they are caught.
+"""
+import json
+import math
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from flow_matching_dit_amd import synth
+from oracle import gr00t_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def tiny_workload(**cfg_kw):
+    """A very small head (fast in the oracle) with the tiny workload's recipe."""
+    cfg = replace(synth.TINY, num_layers=2, hidden=32, num_heads=2, head_dim=16, ff_dim=64,
+                  vl_dim=24, time_freq_dim=16, state_dim=6, action_dim=5, action_horizon=4,
+                  num_categories=3, num_steps=4, precision="fp32")
+    cfg = replace(cfg, **cfg_kw)
+    return synth.Workload("pin_tiny", 900, cfg, batch=3, vl_len=7, id_range=(0, 2),
+                          len_range=(2, 7), image_tokens=4, mask_tail_range=(0, 2))
+
+
+def run(w, weights=None, inputs=None, noise=None, **kw):
+    weights = weights if weights is not None else synth.make_weights(w)
+    inputs = inputs if inputs is not None else synth.make_inputs(w)
+    noise = noise if noise is not None else synth.make_noise(w)
+    return O.get_action(w.cfg.as_dict(), weights, inputs, noise, **kw)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_bf16_rounding_ties_and_library():
+    one = 1.0
+    ulp = 2.0 ** -7
+    vals = np.array([one, one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 2 ** -20,
+                     -(one + ulp / 2), 3.0e-39], np.float32)
+    got = O.round_bf16(vals)
+    assert got[0] == 1.0
+    assert got[1] == 1.0                      # tie -> even (mantissa LSB 0)
+    assert got[2] == one + 2 * ulp            # tie -> even neighbour above
+    assert got[3] == one + ulp                # above half -> up
+    assert got[4] == -1.0
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x), lib)
+
+
+def test_e4m3_codes_match_specification():
+    g = _golden("e4m3_values.json")
+    for code, val in g["codes"].items():
+        d = O.e4m3_decode(np.array([int(code, 16)], np.uint8))[0]
+        assert d == val and np.signbit(d) == np.signbit(val)
+    for code in g["nan_codes"]:
+        assert np.isnan(O.e4m3_decode(np.array([int(code, 16)], np.uint8))[0])
+
+
+def test_e4m3_roundtrip_all_codes_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = O.e4m3_decode(codes)
+    back = O.e4m3_encode(vals)
+    assert np.array_equal(back, codes)
+    pos = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = O.e4m3_encode(mids)
+    lo = np.arange(0x7E)
+    assert np.array_equal(enc, np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8))
+    assert O.e4m3_encode(np.array([1e6, -500.0]))[0] == 0x7E
+    assert O.e4m3_encode(np.array([-500.0]))[0] == 0xFE
+
+
+def test_e4m3_matches_library_cast_in_range():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(50000) * 60).clip(-447, 447).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), lib)
+
+
+def test_e4m3_column_quantisation():
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((3, 40, 24)) * 0.02).astype(np.float32)
+    w[1, :, 5] = 0.0
+    deq, codes, scale = O.quantize_e4m3_columns(w)
+    assert deq.shape == w.shape and scale.shape == (3, 1, 24)
+    amax_idx = np.argmax(np.abs(w), axis=1)
+    for c in range(3):
+        for o in range(24):
+            if c == 1 and o == 5:
+                assert np.all(codes[c, :, o] == 0) and scale[c, 0, o] == 1.0
+                continue
+            assert codes[c, amax_idx[c, o], o] & 0x7F == 0x7E
+    rel = np.abs(deq - w) / np.maximum(np.abs(w), 1e-30)
+    normal = np.abs(w / scale) >= 2.0 ** -6
+    assert rel[normal].max() <= 2.0 ** -4 + 1e-6
+
+
+# ---------------------------------------------------------------- elementwise blocks
+
+def test_layer_norm_statistics():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 64)) * 3 + 2
+    y = O.layer_norm(x)
+    var = x.var(axis=-1)
+    assert np.allclose(y.mean(axis=-1), 0, atol=1e-12)
+    assert np.allclose(y.var(axis=-1), var / (var + O.LN_EPS), rtol=1e-12)
+    g, b = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.allclose(O.layer_norm(x, g, b), y * g + b, atol=1e-12)
+
+
+def test_gelu_textbook_values():
+    assert O.gelu(np.array(0.0)) == 0.0
+    assert abs(O.gelu(np.array(1.0)) - 0.8413447460685429) < 1e-15
+    assert abs(O.gelu(np.array(-1.0)) + 0.15865525393145707) < 1e-15
+    for x in np.linspace(-6, 6, 49):
+        assert abs(O.gelu(np.array(x)) - x * 0.5 * (1 + math.erf(x / math.sqrt(2)))) < 1e-14
+    assert abs(O.gelu(np.array(10.0)) - 10.0) < 1e-12
+
+
+def test_silu_relu():
+    assert O.silu(np.array(0.0)) == 0.0
+    assert abs(O.silu(np.array(2.0)) - 2.0 / (1.0 + math.exp(-2.0))) < 1e-15
+    assert O.relu(np.array(-3.0)) == 0.0 and O.relu(np.array(3.0)) == 3.0
+
+
+def test_sinusoid_values():
+    s0 = O.sinusoid(np.array(0.0), 256)
+    assert np.array_equal(s0[:128], np.zeros(128)) and np.array_equal(s0[128:], np.ones(128))
+    s1 = O.sinusoid(np.array(1.0), 4)     # half = 2: frequencies 1 and 10000^(-1/2) = 0.01
+    assert np.allclose(s1, [math.sin(1), math.sin(0.01), math.cos(1), math.cos(0.01)], atol=1e-15)
+    s = O.sinusoid(np.array(750.0), 64)
+    assert np.allclose(s[:32] ** 2 + s[32:] ** 2, 1.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- per-embodiment linear
+
+def test_category_linear_brute_force_integer_exact():
+    g = _golden("category_linear_example.json")
+    C, din, dout = g["num_categories"], g["input_dim"], g["hidden_dim"]
+    rng = np.random.default_rng(2)
+    W = rng.integers(-3, 4, (C, din, dout)).astype(np.float64)
+    b = rng.integers(-3, 4, (C, dout)).astype(np.float64)
+    x = rng.integers(-3, 4, (4, 2, din)).astype(np.float64)
+    ids = np.array([9, 0, 4, 9])
+    y = O.category_linear(x, W, b, ids)
+    assert y.shape == (4, 2, dout)
+    for bi in range(4):
+        for t in range(2):
+            for o in range(0, dout, 37):
+                ref = b[ids[bi], o]
+                for i in range(din):
+                    ref += x[bi, t, i] * W[ids[bi], i, o]
+                assert y[bi, t, o] == ref
+
+
+# ---------------------------------------------------------------- attention
+
+def _qkv(S=3, L=6, h=2, d=4, seed=3):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((S, h, d)), rng.standard_normal((L, h, d)), rng.standard_normal((L, h, d))
+
+
+def test_attention_closed_forms():
+    q, k, v = _qkv()
+    adm = np.array([1, 0, 1, 1, 0, 1], bool)
+    ones = np.ones_like(v)
+    assert np.allclose(O.attention(q, k, ones, adm), 1.0, atol=1e-14)
+    single = np.zeros(6, bool); single[4] = True
+    out = O.attention(q, k, v, single)
+    assert np.allclose(out, np.broadcast_to(v[4], out.shape), atol=1e-14)
+    out = O.attention(np.zeros_like(q), k, v, adm)
+    assert np.allclose(out, np.broadcast_to(v[adm].mean(axis=0), out.shape), atol=1e-14)
+    assert np.array_equal(O.attention(q, k, v, np.zeros(6, bool)), np.zeros_like(q))
+    perm = np.array([3, 0, 5, 1, 2, 4])
+    assert np.allclose(O.attention(q, k[perm], v[perm], adm[perm]), O.attention(q, k, v, adm))
+
+
+def test_attention_temperature():
+    d = 4
+    q = np.ones((1, 1, d))
+    k = np.stack([np.ones((1, d)), np.zeros((1, d))])       # q.k = 4 and 0
+    v = np.stack([np.ones((1, d)), np.zeros((1, d))])
+    out = O.attention(q, k, v, np.ones(2, bool))
+    e2 = math.exp(4 / math.sqrt(d))
+    assert np.allclose(out, e2 / (e2 + 1), atol=1e-15)
+
+
+# ---------------------------------------------------------------- integrator and schedule
+
+def test_time_grid_matches_page():
+    g = _golden("inference_time_grid.json")
+    t, tau, dt = O.timestep_grid(g["num_inference_timesteps"], g["num_timestep_buckets"])
+    assert dt == g["dt"] and t == g["t_cont"]
+    assert tau == [int(g["num_timestep_buckets"] * tc) for tc in g["t_cont"]] == [0, 250, 500, 750]
+    assert O.timestep_grid(8)[1] == [0, 125, 250, 375, 500, 625, 750, 875]
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 8])
+def test_euler_closed_forms(K):
+    x0 = np.array([0.3, -1.7, 2.0])
+    lam = -0.7
+    got = O.euler(x0, lambda x, k, tau: lam * x, K)
+    assert np.allclose(got, (1 + lam / K) ** K * x0, rtol=1e-14)
+    a = 1.25
+    got = O.euler(x0, lambda x, k, tau: a * (k / K) * np.ones_like(x), K)
+    assert np.allclose(got, x0 + a * (K - 1) / (2 * K), rtol=1e-14)
+    assert np.array_equal(O.euler(x0, lambda x, k, tau: np.zeros_like(x), K), x0)
+
+
+def test_alternate_schedule():
+    g = _golden("alternate_vldit_schedule.json")
+    cfg = {"attend_text_every_n_blocks": g["attend_text_every_n_blocks"]}
+    valid = np.array([1, 1, 1, 1, 0, 1], bool)
+    image = np.array([1, 1, 0, 0, 1, 0], bool)
+    for l, kind in enumerate(g["schedule"]):
+        if kind == "self":
+            assert l % 2 == 1
+            continue
+        m = O.cross_layer_mask(cfg, l, valid, image)
+        exp = valid & ~image if kind == "text" else valid & image
+        assert np.array_equal(m, exp)
+    text = O.cross_layer_mask(cfg, 0, valid, image)
+    img = O.cross_layer_mask(cfg, 2, valid, image)
+    assert np.array_equal(text | img, valid) and not np.any(text & img)
+    assert np.array_equal(O.cross_layer_mask(cfg, 2, valid, None), valid)
+
+
+def test_ada_layer_norm_scale_shift_order():
+    D = 8
+    rng = np.random.default_rng(4)
+    h = rng.standard_normal((2, D))
+    P = {"x.ada.w": np.zeros((D, 2 * D)),
+         "x.ada.b": np.concatenate([np.full(D, 1.0), np.full(D, 3.0)])}
+    out = O.ada_layer_norm(P, "x.", h, rng.standard_normal(D))
+    assert np.allclose(out, 2.0 * O.layer_norm(h) + 3.0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- whole head
+
+def test_shapes_follow_get_action_contract():
+    g = _golden("model_configuration_table.json")
+    w = tiny_workload(action_horizon=g["example_action_pred_shape_tail"][0],
+                      action_dim=g["example_action_pred_shape_tail"][1])
+    y = run(w)
+    assert y.shape == (w.batch, 16, 29)
+    assert np.all(np.isfinite(y))
+
+
+def test_zero_velocity_returns_noise_and_constant_velocity():
+    w = tiny_workload()
+    wt = synth.make_weights(w)
+    inp = synth.make_inputs(w)
+    inp["action_mask"] = None
+    noise = synth.make_noise(w)
+    wt["action_dec.w2"][:] = 0
+    wt["action_dec.b2"][:] = 0
+    assert np.array_equal(run(w, wt, inp, noise), noise.astype(np.float64))
+    wt["action_dec.b2"][:] = 0.5
+    assert np.array_equal(run(w, wt, inp, noise), noise.astype(np.float64) + 0.5)
+
+
+def test_k1_is_one_forward():
+    w = tiny_workload(num_steps=1)
+    wt, inp, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    inp["action_mask"] = None
+    y = run(w, wt, inp, noise)
+    v = O.get_action(w.cfg.as_dict(), wt, inp, noise, return_velocity_at=0)
+    assert np.allclose(y, noise + v, rtol=0, atol=1e-15)
+
+
+def test_masked_vl_tokens_do_not_matter():
+    w = tiny_workload()
+    wt, inp, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    y0 = run(w, wt, inp, noise)
+    inp2 = dict(inp)
+    vl = inp["vl_features"].copy()
+    vl[inp["vl_mask"] == 0] = 77.0
+    inp2["vl_features"] = vl
+    assert np.array_equal(run(w, wt, inp2, noise), y0)
+    vl = inp["vl_features"].copy()
+    b = 0
+    # with two blocks only block 0 cross-attends, to text tokens (valid and not image)
+    j = int(np.flatnonzero(inp["vl_mask"][b] & (1 - inp["image_mask"][b]))[0])
+    vl[b, j] = np.random.default_rng(3).standard_normal(vl.shape[-1]) * 5
+    inp2["vl_features"] = vl
+    y2 = run(w, wt, inp2, noise)
+    assert np.abs(y2[b] - y0[b]).max() > 1e-9 and np.array_equal(y2[1:], y0[1:])
+
+
+def test_batch_independence_and_unused_categories():
+    w = tiny_workload()
+    wt, inp, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    y = run(w, wt, inp, noise)
+    for b in range(w.batch):
+        sub, nz = synth.take_samples(inp, noise, [b])
+        yb = run(replace(w, batch=1), wt, sub, nz)
+        assert np.allclose(yb[0], y[b], rtol=0, atol=1e-13)
+    used = set(inp["embodiment_id"].tolist())
+    wt2 = {k: v.copy() for k, v in wt.items()}
+    for name, v in wt2.items():
+        if v.ndim >= 2 and v.shape[0] == w.cfg.num_categories and (
+                name.startswith(("state_enc.", "action_enc.", "action_dec."))):
+            for c in range(w.cfg.num_categories):
+                if c not in used:
+                    v[c] = 123.0
+    if len(used) < w.cfg.num_categories:
+        assert np.array_equal(run(w, wt2, inp, noise), y)
+
+
+def test_horizon_permutation_equivariance():
+    w = tiny_workload()
+    wt, inp, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    inp["action_mask"] = None
+    y = run(w, wt, inp, noise)
+    perm = np.array([2, 0, 3, 1])
+    yp = run(w, wt, inp, np.ascontiguousarray(noise[:, perm]))
+    assert np.allclose(yp, y[:, perm], rtol=0, atol=1e-12)
+
+
+def test_block_with_zero_output_projections_is_identity():
+    w = tiny_workload()
+    cfg = w.cfg.as_dict()
+    wt = synth.make_weights(w)
+    for l in range(w.cfg.num_layers):
+        for n in ("attn.wo", "attn.bo", "ff.w2", "ff.b2"):
+            wt[f"blocks.{l}.{n}"][:] = 0
+    P = O.effective_params(cfg, wt)
+    rng = np.random.default_rng(9)
+    B, S, D = 2, 5, w.cfg.hidden
+    h = rng.standard_normal((B, S, D))
+    vl = rng.standard_normal((B, 7, w.cfg.vl_dim))
+    valid = np.ones((B, 7), bool)
+    temb = rng.standard_normal(D)
+    for l in range(w.cfg.num_layers):
+        masks = [valid[b] for b in range(B)]
+        assert np.array_equal(O.transformer_block(P, cfg, l, h, vl, masks, temb), h)
+    wt["blocks.0.attn.bo"][:] = 0.25
+    P = O.effective_params(cfg, wt)
+    out = O.transformer_block(P, cfg, 0, h, vl, [valid[b] for b in range(B)], temb)
+    assert np.allclose(out, h + 0.25, atol=1e-14)
+
+
+def test_action_mask_applies_to_final_chunk_only():
+    w = tiny_workload()
+    wt, inp, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    y = run(w, wt, inp, noise)
+    inp2 = dict(inp); inp2["action_mask"] = None
+    y_un = run(w, wt, inp2, noise)
+    assert np.array_equal(y, y_un * inp["action_mask"])
+
+
+def test_fp8_mode_quantises_only_dit_matrices():
+    w = tiny_workload(precision="fp8")
+    wt = synth.make_weights(w)
+    P = O.effective_params(w.cfg.as_dict(), wt)
+    for name, v in wt.items():
+        if O.is_fp8_matrix(name):
+            assert np.array_equal(P[name], O.quantize_e4m3_columns(v)[0])
+            assert name.startswith("blocks.") or name == "out.proj.w"
+        else:
+            assert np.array_equal(P[name], O.round_bf16(v))
+    assert O.is_fp8_matrix("blocks.0.attn.wk") and not O.is_fp8_matrix("blocks.0.ada.w")
+    assert not O.is_fp8_matrix("action_dec.w1")
+
+
+def test_precisions_agree_roughly():
+    w32 = tiny_workload()
+    y32 = run(w32)
+    for prec, tol in (("bf16", 2e-2), ("fp8", 5e-2)):
+        w = tiny_workload(precision=prec)
+        assert O.rel_l2(run(w), y32) < tol

@@ -1,0 +1,127 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches each one.
+
+Each case swaps one oracle function for a subtly wrong version (on the CPU only)
+and runs the pin that is meant to catch it; the pin must fail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import test_oracle as pins
+from oracle import gr00t_oracle as O
+
+
+def _gelu_tanh(x):
+    return 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _attention_no_temperature(q, k, v, admitted):
+    return O.__dict__["_orig_attention"](q * math.sqrt(q.shape[-1]), k, v, admitted)
+
+
+def _ada_swapped(P, prefix, h, temb):
+    D = h.shape[-1]
+    mod = O.linear(O.silu(temb), P[prefix + "ada.w"], P[prefix + "ada.b"])
+    return O.layer_norm(h) * (1.0 + mod[D:]) + mod[:D]
+
+
+def _block_without_residual(P, cfg, l, h, vl, key_masks, temb):
+    return O.__dict__["_orig_block"](P, cfg, l, h, vl, key_masks, temb) - h
+
+
+def _category_linear_no_bias(x, W, b, ids):
+    return np.einsum("bti,bio->bto", x, W[ids])
+
+
+def _category_linear_first_id(x, W, b, ids):
+    return np.einsum("bti,io->bto", x, W[ids[0]]) + b[ids[0]][None, None, :]
+
+
+def _bf16_truncate(a):
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _euler_wrong_dt(x0, vfn, K, buckets=1000):
+    _, tau, _ = O.timestep_grid(K, buckets)
+    x = np.array(x0, dtype=np.float64)
+    for k in range(K):
+        x = x + (1.0 / (K + 1)) * vfn(x, k, tau[k])
+    return x
+
+
+def _grid_shifted(K, buckets=1000):
+    return [(k + 1) / K for k in range(K)], [(buckets * (k + 1)) // K for k in range(K)], 1.0 / K
+
+
+def _mask_swapped(cfg, l, valid, image):
+    if image is None:
+        return valid
+    if l % (2 * cfg["attend_text_every_n_blocks"]) == 0:
+        return valid & image
+    return valid & ~image
+
+
+def _layer_norm_unbiased(x, gamma=None, beta=None, eps=O.LN_EPS):
+    mu = x.mean(axis=-1, keepdims=True)
+    var = x.var(axis=-1, ddof=1, keepdims=True)
+    y = (x - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * gamma
+    if beta is not None:
+        y = y + beta
+    return y
+
+
+def _sinusoid_cos_first(tau, dim):
+    s = O.__dict__["_orig_sinusoid"](tau, dim)
+    half = dim // 2
+    return np.concatenate([s[..., half:], s[..., :half]], axis=-1)
+
+
+def _e4m3_ties_away(v):
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(O._E4M3_POS, mag, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    pick_lo = np.abs(mag - O._E4M3_POS[lo]) < np.abs(O._E4M3_POS[hi] - mag)
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def _velocity_decode_all_rows(P, cfg, vl, valid, image, s, x, tau, ids):
+    temb = O.timestep_encoder(P, cfg, tau)
+    af = O.action_encoder(P, cfg, x, tau, ids)
+    y = O.dit(P, cfg, np.concatenate([af, s], axis=1), vl, valid, image, temb)
+    return O.action_decoder(P, y[:, 1:, :], ids)
+
+
+CASES = [
+    ("gelu", _gelu_tanh, pins.test_gelu_textbook_values),
+    ("attention", _attention_no_temperature, pins.test_attention_temperature),
+    ("ada_layer_norm", _ada_swapped, pins.test_ada_layer_norm_scale_shift_order),
+    ("transformer_block", _block_without_residual,
+     pins.test_block_with_zero_output_projections_is_identity),
+    ("category_linear", _category_linear_no_bias, pins.test_category_linear_brute_force_integer_exact),
+    ("category_linear", _category_linear_first_id, pins.test_category_linear_brute_force_integer_exact),
+    ("round_bf16", _bf16_truncate, pins.test_bf16_rounding_ties_and_library),
+    ("euler", _euler_wrong_dt, lambda: pins.test_euler_closed_forms(4)),
+    ("timestep_grid", _grid_shifted, pins.test_time_grid_matches_page),
+    ("cross_layer_mask", _mask_swapped, pins.test_alternate_schedule),
+    ("layer_norm", _layer_norm_unbiased, pins.test_layer_norm_statistics),
+    ("sinusoid", _sinusoid_cos_first, pins.test_sinusoid_values),
+    ("e4m3_encode", _e4m3_ties_away, pins.test_e4m3_roundtrip_all_codes_and_ties),
+    ("velocity", _velocity_decode_all_rows, pins.test_horizon_permutation_equivariance),
+]
+
+
+@pytest.mark.parametrize("name,bad,pin", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_planted_mistake_is_caught(monkeypatch, name, bad, pin):
+    monkeypatch.setitem(O.__dict__, "_orig_attention", O.attention)
+    monkeypatch.setitem(O.__dict__, "_orig_block", O.transformer_block)
+    monkeypatch.setitem(O.__dict__, "_orig_sinusoid", O.sinusoid)
+    monkeypatch.setattr(O, name, bad)
+    with pytest.raises(AssertionError):
+        pin()

@@ -1,0 +1,979 @@
+// Host runtime of the GR00T action head behind the C ABI of gr00t_head.h.
+//
+// Owns: argument validation (no HIP call before a check passes), the weight
+// registry and packer (fp32 masters -> bf16 round-to-nearest-even or per-column
+// e4m3, transposed to the [out][in] layout the GEMM kernels read), the device
+// arena, the workspace, the per-step tables, and the launch sequence of one
+// get_action call:
+//   prologue  : mask codes, id check, vision-language LayerNorm, the key/value
+//               projection of every cross-attention block (once per call, reused by
+//               all K steps), the state encoder, x0 = noise;
+//   K steps   : action encoder -> state+action tokens -> 32 DiT blocks -> output
+//               adaLN + projection -> decoder with the Euler update fused in;
+//   epilogue  : action_pred = x * action_mask.
+// The K-step part can be captured once per (B, L_pad) into a hipGraph.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gr00t_head.h"
+#include "kernels.h"
+
+using namespace gr00t;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+// ------------------------------------------------------------------ host number formats
+
+uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+float host_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Nearest OCP E4M3 code of a (finite) float, ties to even, magnitudes >= 448 saturate.
+uint8_t host_f32_to_e4m3(float v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0;
+  const float a = std::fabs(v);
+  if (!(a < 448.0f)) return sign | 0x7E;
+  if (a < 0.015625f) {  // below 2^-6: subnormal quantum 2^-9
+    const int m = (int)std::nearbyint(a * 512.0f);  // 0..8; 8 is the smallest normal
+    return sign | (uint8_t)m;
+  }
+  int e;
+  std::frexp(a, &e);  // a in [2^(e-1), 2^e)
+  int E = e - 1;      // -6 .. 8
+  int mq = (int)std::nearbyint(std::ldexp(a, 3 - E));  // 8 .. 16
+  if (mq == 16) {
+    mq = 8;
+    E += 1;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | (mq - 8));
+}
+
+// ------------------------------------------------------------------ weight registry
+
+enum Store { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2 };
+
+struct Piece {           // one packed destination of a loaded tensor
+  size_t off = 0;        // byte offset of the packed data in the arena
+  size_t scale_off = 0;  // byte offset of the per-column scales (ST_FP8)
+  int in_lo = 0, in_n = 0;  // slice of the `in` axis taken (matrices)
+};
+
+struct Spec {
+  std::vector<int64_t> shape;
+  bool matrix = false;   // [.., in, out] linear weight, packed [C][out][in]
+  Store store = ST_F32;  // storage of the packed data (vectors are always fp32)
+  std::vector<Piece> pieces;
+  bool loaded = false;
+  std::vector<uint8_t> staged;  // packed bytes, per piece concatenated (data then scales)
+};
+
+struct LayerOff {
+  size_t wq = 0, bq = 0, sq = 0;  // self: wq region = [Wq;Wk;Wv] (3D x D), biases/scales 3D
+  size_t wo = 0, bo = 0, so = 0;
+  size_t w1 = 0, b1 = 0, s1 = 0;
+  size_t w2 = 0, b2 = 0, s2 = 0;
+};
+
+struct Layout {
+  size_t vlln_g, vlln_b;
+  size_t t_w1, t_b1, t_w2, t_b2;
+  size_t se_w1, se_b1, se_w2, se_b2;
+  size_t ae_w1, ae_b1, ae_w2a, ae_w2t, ae_b2, ae_w3, ae_b3;
+  size_t ada_w, ada_b;
+  std::vector<LayerOff> L;
+  size_t kv_w, kv_b, kv_s;
+  size_t p_w, p_b, p_s;
+  size_t d_w1, d_b1, d_w2, d_b2;
+  size_t total;
+};
+
+struct Ws {  // workspace pointers
+  float* h;
+  void *n, *q, *k, *v, *o, *u, *y, *e1, *e2, *se1, *vln, *kc, *vc;
+  float *x, *s, *vout;
+  uint8_t *code, *bad;
+  int *ids, *iota;
+  float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
+};
+
+}  // namespace
+
+struct gr00t_head {
+  gr00t_config cfg{};
+  int device = 0;
+  std::string err;
+  bool finalized = false;
+  DType act = DT_BF16;
+  std::map<std::string, Spec> specs;
+  std::vector<std::string> order;
+  Layout lay{};
+  char* arena = nullptr;
+  char* wsbase = nullptr;
+  size_t ws_bytes = 0;
+  Ws w{};
+  hipStream_t cap_stream = nullptr;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  uint64_t calls = 0;
+  uint8_t* bad_host = nullptr;      // pinned copy of the per-sample bad-id flags
+  hipEvent_t bad_event = nullptr;
+  int bad_pending_B = 0;
+  std::vector<int> tau;
+};
+
+namespace {
+
+int fail(gr00t_head* h, int code, const std::string& msg) {
+  if (h) h->err = msg;
+  return code;
+}
+
+size_t act_bytes(const gr00t_head* h) { return h->act == DT_F32 ? 4 : 2; }
+
+
+std::string shape_str(const std::vector<int64_t>& s) {
+  std::string r = "[";
+  for (size_t i = 0; i < s.size(); ++i) r += (i ? "," : "") + std::to_string(s[i]);
+  return r + "]";
+}
+
+int check_config(const gr00t_config* c, std::string& why) {
+  if (!c) { why = "config is NULL"; return GR00T_E_INVALID_ARG; }
+  auto bad = [&](const char* m) { why = m; return GR00T_E_INVALID_ARG; };
+  if (c->num_layers < 1) return bad("num_layers must be >= 1");
+  if (c->num_heads < 1 || c->head_dim < 16 || c->head_dim > 64 || c->head_dim % 16)
+    return bad("head_dim must be a multiple of 16 in [16, 64]");
+  if (c->hidden != c->num_heads * c->head_dim) return bad("hidden must equal num_heads * head_dim");
+  if (c->hidden > 2048 || c->hidden % 16) return bad("hidden must be a multiple of 16, at most 2048");
+  if (c->vl_dim < 16 || c->vl_dim > 2048 || c->vl_dim % 16) return bad("vl_dim must be a multiple of 16 in [16, 2048]");
+  if (c->ff_dim < 16 || c->ff_dim % 16) return bad("ff_dim must be a positive multiple of 16");
+  if (c->state_dim < 1) return bad("state_dim must be >= 1");
+  if (c->action_dim < 1) return bad("action_dim must be >= 1");
+  if (c->action_horizon < 1 || c->action_horizon + 1 > 65) return bad("action_horizon must be in [1, 64]");
+  if (c->num_categories < 1) return bad("num_categories must be >= 1");
+  if (c->num_steps < 1 || c->num_steps > 64) return bad("num_steps must be in [1, 64]");
+  if (c->num_timestep_buckets < 1) return bad("num_timestep_buckets must be >= 1");
+  if (c->attend_text_every_n_blocks < 1) return bad("attend_text_every_n_blocks must be >= 1");
+  if (c->time_freq_dim < 2 || c->time_freq_dim % 2) return bad("time_freq_dim must be even and >= 2");
+  if (c->max_batch < 1 || c->max_vl_len < 1) return bad("max_batch and max_vl_len must be >= 1");
+  if (!(c->weight_dtype == GR00T_F32 || c->weight_dtype == GR00T_BF16 || c->weight_dtype == GR00T_FP8_E4M3))
+    return bad("weight_dtype must be F32, BF16 or FP8_E4M3");
+  if (!(c->act_dtype == GR00T_F32 || c->act_dtype == GR00T_BF16)) return bad("act_dtype must be F32 or BF16");
+  if ((c->weight_dtype == GR00T_F32) != (c->act_dtype == GR00T_F32))
+    return bad("F32 weights go with F32 activations, BF16/FP8 weights with BF16 activations");
+  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH)) return bad("unknown flag bits");
+  return GR00T_OK;
+}
+
+bool is_fp8_name(const std::string& n) {
+  if (n == "out.proj.w") return true;
+  if (n.rfind("blocks.", 0) != 0) return false;
+  static const char* suf[] = {"attn.wq", "attn.wk", "attn.wv", "attn.wo", "ff.w1", "ff.w2"};
+  for (const char* s : suf) {
+    const size_t ls = std::strlen(s);
+    if (n.size() >= ls && n.compare(n.size() - ls, ls, s) == 0) return true;
+  }
+  return false;
+}
+
+// Build the canonical weight list and the arena layout for the config.
+void build_specs(gr00t_head* h) {
+  const gr00t_config& c = h->cfg;
+  const int64_t D = c.hidden, F = c.ff_dim, C = c.num_categories, E = c.vl_dim, Nl = c.num_layers;
+  const int Nc = (int)((Nl + 1) / 2);
+  const Store mat = c.weight_dtype == GR00T_F32 ? ST_F32 : ST_BF16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  auto elt = [&](Store s) -> size_t { return s == ST_F32 ? 4 : (s == ST_BF16 ? 2 : 1); };
+  auto add = [&](const std::string& name, std::vector<int64_t> shape, bool matrix) -> Spec& {
+    Spec& s = h->specs[name];
+    s.shape = std::move(shape);
+    s.matrix = matrix;
+    s.store = matrix ? ((c.weight_dtype == GR00T_FP8_E4M3 && is_fp8_name(name)) ? ST_FP8 : mat) : ST_F32;
+    h->order.push_back(name);
+    return s;
+  };
+  auto vec = [&](const std::string& name, std::vector<int64_t> shape, size_t at) {
+    Spec& s = add(name, shape, false);
+    Piece p;
+    p.off = at;
+    s.pieces.push_back(p);
+  };
+  auto matp = [&](const std::string& name, std::vector<int64_t> shape, size_t at, size_t sat, int in_lo, int in_n) {
+    Spec& s = h->specs[name];
+    if (s.shape.empty()) add(name, shape, true);
+    Piece p;
+    p.off = at;
+    p.scale_off = sat;
+    p.in_lo = in_lo;
+    p.in_n = in_n;
+    h->specs[name].pieces.push_back(p);
+  };
+  Layout& L = h->lay;
+  L.L.resize(Nl);
+  const size_t me = elt(mat);
+  const auto mstore = [&](const std::string& n) { return (c.weight_dtype == GR00T_FP8_E4M3 && is_fp8_name(n)) ? ST_FP8 : mat; };
+
+  L.vlln_g = take(E * 4); vec("vlln.gamma", {E}, L.vlln_g);
+  L.vlln_b = take(E * 4); vec("vlln.beta", {E}, L.vlln_b);
+  L.t_w1 = take((size_t)c.time_freq_dim * D * me); matp("time.w1", {c.time_freq_dim, D}, L.t_w1, 0, 0, c.time_freq_dim);
+  L.t_b1 = take(D * 4); vec("time.b1", {D}, L.t_b1);
+  L.t_w2 = take(D * D * me); matp("time.w2", {D, D}, L.t_w2, 0, 0, (int)D);
+  L.t_b2 = take(D * 4); vec("time.b2", {D}, L.t_b2);
+  L.se_w1 = take(C * c.state_dim * D * me); matp("state_enc.w1", {C, c.state_dim, D}, L.se_w1, 0, 0, c.state_dim);
+  L.se_b1 = take(C * D * 4); vec("state_enc.b1", {C, D}, L.se_b1);
+  L.se_w2 = take(C * D * D * me); matp("state_enc.w2", {C, D, D}, L.se_w2, 0, 0, (int)D);
+  L.se_b2 = take(C * D * 4); vec("state_enc.b2", {C, D}, L.se_b2);
+  L.ae_w1 = take(C * c.action_dim * D * me); matp("action_enc.w1", {C, c.action_dim, D}, L.ae_w1, 0, 0, c.action_dim);
+  L.ae_b1 = take(C * D * 4); vec("action_enc.b1", {C, D}, L.ae_b1);
+  L.ae_w2a = take(C * D * D * me);
+  L.ae_w2t = take(C * D * D * me);
+  matp("action_enc.w2", {C, 2 * D, D}, L.ae_w2a, 0, 0, (int)D);
+  matp("action_enc.w2", {C, 2 * D, D}, L.ae_w2t, 0, (int)D, (int)D);
+  L.ae_b2 = take(C * D * 4); vec("action_enc.b2", {C, D}, L.ae_b2);
+  L.ae_w3 = take(C * D * D * me); matp("action_enc.w3", {C, D, D}, L.ae_w3, 0, 0, (int)D);
+  L.ae_b3 = take(C * D * 4); vec("action_enc.b3", {C, D}, L.ae_b3);
+  // adaLN linears of all blocks and of the output norm, concatenated along N.
+  L.ada_w = take((size_t)(Nl + 1) * 2 * D * D * me);
+  L.ada_b = take((size_t)(Nl + 1) * 2 * D * 4);
+  // cross key/value projections of all cross blocks, concatenated along N.
+  const Store kvs = mstore("blocks.0.attn.wk");
+  L.kv_w = take((size_t)Nc * 2 * D * E * elt(kvs));
+  L.kv_b = take((size_t)Nc * 2 * D * 4);
+  L.kv_s = take((size_t)Nc * 2 * D * 4);
+  for (int l = 0; l < Nl; ++l) {
+    const std::string p = "blocks." + std::to_string(l) + ".";
+    LayerOff& lo = L.L[l];
+    const size_t esz = elt(mstore(p + "attn.wq"));
+    matp(p + "ada.w", {D, 2 * D}, L.ada_w + (size_t)l * 2 * D * D * me, 0, 0, (int)D);
+    vec(p + "ada.b", {2 * D}, L.ada_b + (size_t)l * 2 * D * 4);
+    const bool self = (l % 2) == 1;
+    const int nq = self ? 3 : 1;
+    lo.wq = take((size_t)nq * D * D * esz);
+    lo.bq = take((size_t)nq * D * 4);
+    lo.sq = take((size_t)nq * D * 4);
+    matp(p + "attn.wq", {D, D}, lo.wq, lo.sq, 0, (int)D);
+    vec(p + "attn.bq", {D}, lo.bq);
+    if (self) {
+      matp(p + "attn.wk", {D, D}, lo.wq + (size_t)D * D * esz, lo.sq + D * 4, 0, (int)D);
+      vec(p + "attn.bk", {D}, lo.bq + D * 4);
+      matp(p + "attn.wv", {D, D}, lo.wq + (size_t)2 * D * D * esz, lo.sq + 2 * D * 4, 0, (int)D);
+      vec(p + "attn.bv", {D}, lo.bq + 2 * D * 4);
+    } else {
+      const int ci = l / 2;
+      const size_t kesz = elt(kvs);
+      matp(p + "attn.wk", {E, D}, L.kv_w + (size_t)(2 * ci) * D * E * kesz, L.kv_s + (size_t)(2 * ci) * D * 4, 0,
+           (int)E);
+      vec(p + "attn.bk", {D}, L.kv_b + (size_t)(2 * ci) * D * 4);
+      matp(p + "attn.wv", {E, D}, L.kv_w + (size_t)(2 * ci + 1) * D * E * kesz,
+           L.kv_s + (size_t)(2 * ci + 1) * D * 4, 0, (int)E);
+      vec(p + "attn.bv", {D}, L.kv_b + (size_t)(2 * ci + 1) * D * 4);
+    }
+    lo.wo = take((size_t)D * D * esz); lo.bo = take(D * 4); lo.so = take(D * 4);
+    matp(p + "attn.wo", {D, D}, lo.wo, lo.so, 0, (int)D);
+    vec(p + "attn.bo", {D}, lo.bo);
+    lo.w1 = take((size_t)F * D * esz); lo.b1 = take(F * 4); lo.s1 = take(F * 4);
+    matp(p + "ff.w1", {D, F}, lo.w1, lo.s1, 0, (int)D);
+    vec(p + "ff.b1", {F}, lo.b1);
+    lo.w2 = take((size_t)D * F * esz); lo.b2 = take(D * 4); lo.s2 = take(D * 4);
+    matp(p + "ff.w2", {F, D}, lo.w2, lo.s2, 0, (int)F);
+    vec(p + "ff.b2", {D}, lo.b2);
+  }
+  matp("out.ada.w", {D, 2 * D}, L.ada_w + (size_t)Nl * 2 * D * D * me, 0, 0, (int)D);
+  vec("out.ada.b", {2 * D}, L.ada_b + (size_t)Nl * 2 * D * 4);
+  const size_t pe = elt(mstore("out.proj.w"));
+  L.p_w = take(D * D * pe); L.p_b = take(D * 4); L.p_s = take(D * 4);
+  matp("out.proj.w", {D, D}, L.p_w, L.p_s, 0, (int)D);
+  vec("out.proj.b", {D}, L.p_b);
+  L.d_w1 = take(C * D * D * me); matp("action_dec.w1", {C, D, D}, L.d_w1, 0, 0, (int)D);
+  L.d_b1 = take(C * D * 4); vec("action_dec.b1", {C, D}, L.d_b1);
+  L.d_w2 = take(C * D * c.action_dim * me); matp("action_dec.w2", {C, D, c.action_dim}, L.d_w2, 0, 0, (int)D);
+  L.d_b2 = take(C * c.action_dim * 4); vec("action_dec.b2", {C, (int64_t)c.action_dim}, L.d_b2);
+  L.total = off;
+}
+
+// Pack a loaded tensor (fp32 values or raw bf16 bits) into its pieces.
+void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
+  auto val = [&](size_t i) -> float {
+    if (dt == GR00T_F32) return ((const float*)data)[i];
+    return host_bf16_to_f32(((const uint16_t*)data)[i]);
+  };
+  size_t numel = 1;
+  for (auto d : s.shape) numel *= (size_t)d;
+  s.staged.clear();
+  if (!s.matrix) {
+    s.staged.resize(numel * 4);
+    float* o = (float*)s.staged.data();
+    const bool keep32 = h->cfg.weight_dtype == GR00T_F32;
+    for (size_t i = 0; i < numel; ++i) o[i] = keep32 ? val(i) : host_bf16_to_f32(host_f32_to_bf16(val(i)));
+    return;
+  }
+  const size_t nd = s.shape.size();
+  const int64_t C = nd == 3 ? s.shape[0] : 1, IN = s.shape[nd - 2], OUT = s.shape[nd - 1];
+  for (const Piece& p : s.pieces) {
+    const int64_t in_n = p.in_n;
+    const size_t base = s.staged.size();
+    if (s.store == ST_F32) {
+      s.staged.resize(base + (size_t)C * OUT * in_n * 4);
+      float* o = (float*)(s.staged.data() + base);
+      for (int64_t cc = 0; cc < C; ++cc)
+        for (int64_t oo = 0; oo < OUT; ++oo)
+          for (int64_t i = 0; i < in_n; ++i) o[(cc * OUT + oo) * in_n + i] = val((cc * IN + p.in_lo + i) * OUT + oo);
+    } else if (s.store == ST_BF16) {
+      s.staged.resize(base + (size_t)C * OUT * in_n * 2);
+      uint16_t* o = (uint16_t*)(s.staged.data() + base);
+      for (int64_t cc = 0; cc < C; ++cc)
+        for (int64_t oo = 0; oo < OUT; ++oo)
+          for (int64_t i = 0; i < in_n; ++i)
+            o[(cc * OUT + oo) * in_n + i] = dt == GR00T_BF16
+                                                ? ((const uint16_t*)data)[(cc * IN + p.in_lo + i) * OUT + oo]
+                                                : host_f32_to_bf16(val((cc * IN + p.in_lo + i) * OUT + oo));
+    } else {  // e4m3 with one fp32 scale per output column: codes then scales
+      s.staged.resize(base + (size_t)C * OUT * in_n + (size_t)C * OUT * 4);
+      uint8_t* o = s.staged.data() + base;
+      float* sc = (float*)(s.staged.data() + base + (size_t)C * OUT * in_n);
+      for (int64_t cc = 0; cc < C; ++cc)
+        for (int64_t oo = 0; oo < OUT; ++oo) {
+          float amax = 0.0f;
+          for (int64_t i = 0; i < in_n; ++i) amax = std::fmax(amax, std::fabs(val((cc * IN + p.in_lo + i) * OUT + oo)));
+          const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+          sc[cc * OUT + oo] = scale;
+          for (int64_t i = 0; i < in_n; ++i)
+            o[(cc * OUT + oo) * in_n + i] = host_f32_to_e4m3(val((cc * IN + p.in_lo + i) * OUT + oo) / scale);
+        }
+    }
+  }
+}
+
+#define HIPCHK(h, expr)                                                                                   \
+  do {                                                                                                    \
+    hipError_t e__ = (expr);                                                                              \
+    if (e__ != hipSuccess)                                                                                \
+      return fail((h), GR00T_E_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e__));           \
+  } while (0)
+
+template <typename T>
+T* at(gr00t_head* h, size_t off) {
+  return (T*)(h->arena + off);
+}
+
+// ------------------------------------------------------------------ GEMM dispatch
+
+GemmArgs ga(const void* A, long lda, int rows, int N, int K) {
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.rows = rows;
+  a.N = N;
+  a.K = K;
+  a.groups = 1;
+  return a;
+}
+
+Epi ep_store(void* out, bool f32, long ld, int act = ACT_NONE) {
+  Epi e{};
+  e.kind = EPI_STORE;
+  e.act = act;
+  e.out = out;
+  e.out_f32 = f32 ? 1 : 0;
+  e.out_ld = ld;
+  return e;
+}
+
+hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s) {
+  if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0)
+    return launch_gemm_mfma(a, e, wt, s);
+  return launch_gemm_valu(a, e, at, wt, s);
+}
+
+// ------------------------------------------------------------------ tables (finalize)
+
+int build_tables(gr00t_head* h, hipStream_t s) {
+  const gr00t_config& c = h->cfg;
+  const int D = c.hidden, K = c.num_steps, Nl = c.num_layers, C = c.num_categories, T = c.time_freq_dim;
+  const Layout& L = h->lay;
+  const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
+  h->tau.resize(K);
+  for (int k = 0; k < K; ++k) h->tau[k] = (int)(((int64_t)c.num_timestep_buckets * k) / K);
+  HIPCHK(h, launch_sinusoid(h->tau.data(), K, T, h->w.sin_t, s));
+  HIPCHK(h, launch_sinusoid(h->tau.data(), K, D, h->w.tauemb, s));
+  // temb = W2 SiLU(W1 sin256(tau) + b1) + b2
+  {
+    GemmArgs a = ga(h->w.sin_t, T, K, D, T);
+    a.W = at<void>(h, L.t_w1);
+    a.bias = at<float>(h, L.t_b1);
+    HIPCHK(h, launch_gemm_valu(a, ep_store(h->w.t1, true, D, ACT_SILU), DT_F32, mw, s));
+    a = ga(h->w.t1, D, K, D, D);
+    a.W = at<void>(h, L.t_w2);
+    a.bias = at<float>(h, L.t_b2);
+    HIPCHK(h, launch_gemm_valu(a, ep_store(h->w.temb, true, D), DT_F32, mw, s));
+  }
+  HIPCHK(h, launch_silu(h->w.temb, h->w.stemb, (long)K * D, s));
+  // [scale | shift] of every block and the output norm: ada[k][l][2D]
+  {
+    GemmArgs a = ga(h->w.stemb, D, K, (Nl + 1) * 2 * D, D);
+    a.W = at<void>(h, L.ada_w);
+    a.bias = at<float>(h, L.ada_b);
+    HIPCHK(h, launch_gemm_valu(a, ep_store(h->w.ada, true, (long)(Nl + 1) * 2 * D), DT_F32, mw, s));
+  }
+  // timestep half of the action encoder's second linear, with its bias: c2tab[k][cat][D]
+  {
+    GemmArgs a = ga(h->w.tauemb, D, K, D, D);
+    a.W = at<void>(h, L.ae_w2t);
+    a.w_cstride = (long)D * D;
+    a.bias = at<float>(h, L.ae_b2);
+    a.b_cstride = D;
+    a.ids = h->w.iota;
+    a.groups = C;
+    a.a_gstride = 0;
+    Epi e = ep_store(h->w.c2tab, true, (long)C * D);
+    e.out_gstride = 0;
+    // group g writes columns of category g: offset the output per group via out_row_off
+    // is not expressible with a shared row stride, so launch per category.
+    for (int cat = 0; cat < C; ++cat) {
+      GemmArgs ac = a;
+      ac.groups = 1;
+      ac.ids = h->w.iota + cat;
+      Epi ec = e;
+      ec.out = h->w.c2tab + (size_t)cat * D;
+      HIPCHK(h, launch_gemm_valu(ac, ec, DT_F32, mw, s));
+    }
+  }
+  return GR00T_OK;
+}
+
+// ------------------------------------------------------------------ the launch sequence
+
+int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
+  const gr00t_config& c = h->cfg;
+  const int B = in->batch, L = in->vl_len, D = c.hidden, E = c.vl_dim, Nc = (c.num_layers + 1) / 2;
+  const Layout& lay = h->lay;
+  const DType A = h->act;
+  const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
+  const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
+  HIPCHK(h, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
+  HIPCHK(h, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
+  HIPCHK(h, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
+                             at<float>(h, lay.vlln_b), nullptr, s));
+  {  // keys and values of every cross block: [B*L, E] x [Nc*2D, E]^T -> head-major caches
+    GemmArgs a = ga(h->w.vln, E, B * L, Nc * 2 * D, E);
+    a.W = at<void>(h, lay.kv_w);
+    a.bias = at<float>(h, lay.kv_b);
+    a.wscale = kvw == DT_FP8 ? at<float>(h, lay.kv_s) : nullptr;
+    Epi e{};
+    e.kind = EPI_HEADS;
+    e.out_f32 = A == DT_F32;
+    e.heads[0] = h->w.kc;
+    e.heads[1] = h->w.vc;
+    e.nwhich = 2;
+    e.width = D;
+    e.nh = c.num_heads;
+    e.hd = c.head_dim;
+    e.pos_per_b = L;
+    e.layer_stride = (long)B * L * D;
+    HIPCHK(h, gemm(h, a, e, A, kvw, s));
+  }
+  {  // state encoder: one token per sample
+    GemmArgs a = ga(in->state, c.state_dim, 1, D, c.state_dim);
+    a.groups = B;
+    a.a_gstride = 1;
+    a.ids = h->w.ids;
+    a.W = at<void>(h, lay.se_w1);
+    a.w_cstride = (long)D * c.state_dim;
+    a.bias = at<float>(h, lay.se_b1);
+    a.b_cstride = D;
+    Epi e = ep_store(h->w.se1, A == DT_F32, D, ACT_RELU);
+    e.out_gstride = 1;
+    HIPCHK(h, gemm(h, a, e, DT_F32, mw, s));
+    a = ga(h->w.se1, D, 1, D, D);
+    a.groups = B;
+    a.a_gstride = 1;
+    a.ids = h->w.ids;
+    a.W = at<void>(h, lay.se_w2);
+    a.w_cstride = (long)D * D;
+    a.bias = at<float>(h, lay.se_b2);
+    a.b_cstride = D;
+    e = ep_store(h->w.s, true, D);
+    e.out_gstride = 1;
+    HIPCHK(h, gemm(h, a, e, A, mw, s));
+    if (in->state_features_out)
+      HIPCHK(h, launch_copy_rows(h->w.s, D, in->state_features_out, D, 1, 0, B, D, s));
+  }
+  const long nx = (long)B * c.action_horizon * c.action_dim;
+  HIPCHK(h, launch_init_noise(in->noise, h->w.x, nx, c.noise_seed, h->calls, s));
+  return GR00T_OK;
+}
+
+// Enqueue Euler steps [k0, k1). euler = false writes v of step k0 to w.vout instead.
+int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream_t s) {
+  const gr00t_config& c = h->cfg;
+  const int D = c.hidden, F = c.ff_dim, H = c.action_horizon, S = H + 1, Adim = c.action_dim, Nl = c.num_layers;
+  const int C = c.num_categories, nh = c.num_heads, hd = c.head_dim;
+  const Layout& lay = h->lay;
+  const DType A = h->act;
+  const bool f32 = A == DT_F32;
+  const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
+  const DType dw = c.weight_dtype == GR00T_FP8_E4M3 ? DT_FP8 : mw;  // DiT matrices
+  const long M = (long)B * S;
+  const size_t ab = act_bytes(h);
+  (void)C;
+  for (int k = k0; k < k1; ++k) {
+    // ---- action encoder: a = W1 x + b1; z = swish(W2a a + [W2t tau_emb + b2]); h[1:] = W3 z + b3
+    {
+      GemmArgs a = ga(h->w.x, Adim, H, D, Adim);
+      a.groups = B;
+      a.a_gstride = H;
+      a.ids = h->w.ids;
+      a.W = at<void>(h, lay.ae_w1);
+      a.w_cstride = (long)D * Adim;
+      a.bias = at<float>(h, lay.ae_b1);
+      a.b_cstride = D;
+      Epi e = ep_store(h->w.e1, f32, D);
+      e.out_gstride = H;
+      HIPCHK(h, gemm(h, a, e, DT_F32, mw, s));
+      a = ga(h->w.e1, D, H, D, D);
+      a.groups = B;
+      a.a_gstride = H;
+      a.ids = h->w.ids;
+      a.W = at<void>(h, lay.ae_w2a);
+      a.w_cstride = (long)D * D;
+      e = ep_store(h->w.e2, f32, D, ACT_SILU);
+      e.out_gstride = H;
+      e.add_tab = h->w.c2tab + (size_t)k * c.num_categories * D;
+      e.add_cstride = D;
+      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      a = ga(h->w.e2, D, H, D, D);
+      a.groups = B;
+      a.a_gstride = H;
+      a.ids = h->w.ids;
+      a.W = at<void>(h, lay.ae_w3);
+      a.w_cstride = (long)D * D;
+      a.bias = at<float>(h, lay.ae_b3);
+      a.b_cstride = D;
+      e = ep_store(h->w.h, true, D);
+      e.out_gstride = S;
+      e.out_row_off = 1;
+      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      HIPCHK(h, launch_copy_rows(h->w.s, D, h->w.h, D, S, 0, B, D, s));
+    }
+    // ---- DiT blocks
+    for (int l = 0; l < Nl; ++l) {
+      const LayerOff& lo = lay.L[l];
+      const bool self = (l % 2) == 1;
+      const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + l) * 2 * D;
+      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      {
+        GemmArgs a = ga(h->w.n, D, (int)M, (self ? 3 : 1) * D, D);
+        a.W = at<void>(h, lo.wq);
+        a.bias = at<float>(h, lo.bq);
+        a.wscale = dw == DT_FP8 ? at<float>(h, lo.sq) : nullptr;
+        Epi e{};
+        e.kind = EPI_HEADS;
+        e.out_f32 = f32;
+        e.heads[0] = h->w.q;
+        e.heads[1] = h->w.k;
+        e.heads[2] = h->w.v;
+        e.nwhich = self ? 3 : 1;
+        e.width = D;
+        e.nh = nh;
+        e.hd = hd;
+        e.pos_per_b = S;
+        e.layer_stride = 0;
+        HIPCHK(h, gemm(h, a, e, A, dw, s));
+      }
+      AttnArgs at_{};
+      at_.q = h->w.q;
+      at_.o = h->w.o;
+      at_.B = B;
+      at_.S = S;
+      at_.nh = nh;
+      at_.hd = hd;
+      if (self) {
+        at_.k = h->w.k;
+        at_.v = h->w.v;
+        at_.Lk = S;
+        at_.mask = nullptr;
+      } else {
+        const size_t ci = (size_t)(l / 2);
+        at_.k = (const char*)h->w.kc + ci * (size_t)B * L * D * ab;
+        at_.v = (const char*)h->w.vc + ci * (size_t)B * L * D * ab;
+        at_.Lk = L;
+        at_.mask = h->w.code;
+        at_.mask_bit = (l % (2 * c.attend_text_every_n_blocks) == 0) ? 1 : 2;
+      }
+      HIPCHK(h, launch_attention(at_, A, s));
+      {
+        GemmArgs a = ga(h->w.o, D, (int)M, D, D);
+        a.W = at<void>(h, lo.wo);
+        a.bias = at<float>(h, lo.bo);
+        a.wscale = dw == DT_FP8 ? at<float>(h, lo.so) : nullptr;
+        Epi e = ep_store(h->w.h, true, D);
+        e.kind = EPI_RESID_ADD;
+        HIPCHK(h, gemm(h, a, e, A, dw, s));
+      }
+      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, nullptr, s));
+      {
+        GemmArgs a = ga(h->w.n, D, (int)M, F, D);
+        a.W = at<void>(h, lo.w1);
+        a.bias = at<float>(h, lo.b1);
+        a.wscale = dw == DT_FP8 ? at<float>(h, lo.s1) : nullptr;
+        HIPCHK(h, gemm(h, a, ep_store(h->w.u, f32, F, ACT_GELU), A, dw, s));
+        a = ga(h->w.u, F, (int)M, D, F);
+        a.W = at<void>(h, lo.w2);
+        a.bias = at<float>(h, lo.b2);
+        a.wscale = dw == DT_FP8 ? at<float>(h, lo.s2) : nullptr;
+        Epi e = ep_store(h->w.h, true, D);
+        e.kind = EPI_RESID_ADD;
+        HIPCHK(h, gemm(h, a, e, A, dw, s));
+      }
+    }
+    // ---- output adaLN + projection, then decoder and Euler update
+    {
+      const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + Nl) * 2 * D;
+      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      GemmArgs a = ga(h->w.n, D, (int)M, D, D);
+      a.W = at<void>(h, lay.p_w);
+      a.bias = at<float>(h, lay.p_b);
+      a.wscale = dw == DT_FP8 ? at<float>(h, lay.p_s) : nullptr;
+      HIPCHK(h, gemm(h, a, ep_store(h->w.y, f32, D), A, dw, s));
+      a = ga(h->w.y, D, H, D, D);
+      a.groups = B;
+      a.a_gstride = S;
+      a.a_row_off = 1;
+      a.ids = h->w.ids;
+      a.W = at<void>(h, lay.d_w1);
+      a.w_cstride = (long)D * D;
+      a.bias = at<float>(h, lay.d_b1);
+      a.b_cstride = D;
+      Epi e = ep_store(h->w.e1, f32, D, ACT_RELU);
+      e.out_gstride = H;
+      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      a = ga(h->w.e1, D, H, Adim, D);
+      a.groups = B;
+      a.a_gstride = H;
+      a.ids = h->w.ids;
+      a.W = at<void>(h, lay.d_w2);
+      a.w_cstride = (long)Adim * D;
+      a.bias = at<float>(h, lay.d_b2);
+      a.b_cstride = Adim;
+      if (euler) {
+        e = ep_store(h->w.x, true, Adim);
+        e.kind = EPI_EULER;
+        e.dt = 1.0f / (float)c.num_steps;
+      } else {
+        e = ep_store(h->w.vout, true, Adim);
+      }
+      e.out_gstride = H;
+      HIPCHK(h, gemm(h, a, e, A, mw, s));
+    }
+  }
+  return GR00T_OK;
+}
+
+int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (!in) return fail(h, GR00T_E_INVALID_ARG, "inputs is NULL");
+  if (!out) return fail(h, GR00T_E_INVALID_ARG, "output pointer is NULL");
+  if (in->batch < 1 || in->batch > h->cfg.max_batch)
+    return fail(h, GR00T_E_SHAPE, "batch " + std::to_string(in->batch) + " outside [1, max_batch=" +
+                                      std::to_string(h->cfg.max_batch) + "]");
+  if (in->vl_len < 1 || in->vl_len > h->cfg.max_vl_len)
+    return fail(h, GR00T_E_SHAPE, "vl_len " + std::to_string(in->vl_len) + " outside [1, max_vl_len=" +
+                                      std::to_string(h->cfg.max_vl_len) + "]");
+  if (!in->vl_features) return fail(h, GR00T_E_INVALID_ARG, "vl_features is NULL");
+  if (!in->state) return fail(h, GR00T_E_INVALID_ARG, "state is NULL");
+  if (!in->embodiment_id) return fail(h, GR00T_E_INVALID_ARG, "embodiment_id is NULL");
+  if (!h->finalized) return fail(h, GR00T_E_NOT_FINALIZED, "handle is not finalized");
+  return GR00T_OK;
+}
+
+// Strict-mode id check on the host, and the deferred report of bad ids seen on the device.
+int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
+  if (h->bad_pending_B > 0 && hipEventQuery(h->bad_event) == hipSuccess) {
+    const int nb = h->bad_pending_B;
+    h->bad_pending_B = 0;
+    for (int b = 0; b < nb; ++b)
+      if (h->bad_host[b])
+        return fail(h, GR00T_E_DEVICE_ERROR, "a previous call met an embodiment id outside [0, num_categories) "
+                                             "at sample " + std::to_string(b) + "; its rows were set to NaN");
+  }
+  if (h->cfg.flags & GR00T_FLAG_STRICT) {
+    std::vector<int32_t> ids(in->batch);
+    HIPCHK(h, hipMemcpyAsync(ids.data(), in->embodiment_id, sizeof(int32_t) * in->batch, hipMemcpyDeviceToHost, s));
+    HIPCHK(h, hipStreamSynchronize(s));
+    for (int b = 0; b < in->batch; ++b)
+      if (ids[b] < 0 || ids[b] >= h->cfg.num_categories)
+        return fail(h, GR00T_E_EMBODIMENT, "embodiment_id[" + std::to_string(b) + "] = " + std::to_string(ids[b]) +
+                                               " outside [0, " + std::to_string(h->cfg.num_categories) + ")");
+  }
+  return GR00T_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+int gr00t_create(const gr00t_config* cfg, int device, gr00t_head** out) {
+  g_create_error.clear();
+  if (!out) {
+    g_create_error = "out is NULL";
+    return GR00T_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  std::string why;
+  int rc = check_config(cfg, why);
+  if (rc != GR00T_OK) {
+    g_create_error = why;
+    return rc;
+  }
+  if (device < 0) {
+    g_create_error = "device must be >= 0";
+    return GR00T_E_INVALID_ARG;
+  }
+  gr00t_head* h = new (std::nothrow) gr00t_head();
+  if (!h) {
+    g_create_error = "out of host memory";
+    return GR00T_E_OOM;
+  }
+  h->cfg = *cfg;
+  h->device = device;
+  h->act = cfg->act_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
+  build_specs(h);
+  *out = h;
+  return GR00T_OK;
+}
+
+int gr00t_load_weights(gr00t_head* h, const char* name, const void* host_data, gr00t_dtype dtype,
+                       const int64_t* shape, int ndim) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (h->finalized) return fail(h, GR00T_E_NOT_FINALIZED, "weights cannot be loaded after finalize");
+  if (!name || !host_data || (!shape && ndim > 0) || ndim < 0)
+    return fail(h, GR00T_E_INVALID_ARG, "name, host_data and shape must be non-NULL");
+  auto it = h->specs.find(name);
+  if (it == h->specs.end()) return fail(h, GR00T_E_UNKNOWN_WEIGHT, std::string("unknown weight '") + name + "'");
+  Spec& s = it->second;
+  std::vector<int64_t> got(shape, shape + ndim);
+  if (got != s.shape)
+    return fail(h, GR00T_E_SHAPE, std::string("weight '") + name + "' has shape " + shape_str(got) + ", expected " +
+                                      shape_str(s.shape));
+  if (dtype != GR00T_F32 && dtype != GR00T_BF16)
+    return fail(h, GR00T_E_INVALID_ARG, std::string("weight '") + name + "': dtype must be F32 or BF16");
+  if (dtype == GR00T_BF16 && s.store != ST_BF16)
+    return fail(h, GR00T_E_INVALID_ARG, std::string("weight '") + name +
+                                            "': BF16 input is accepted only for tensors stored as bf16 matrices");
+  try {
+    pack(h, s, host_data, dtype);
+  } catch (const std::bad_alloc&) {
+    return fail(h, GR00T_E_OOM, "out of host memory while packing '" + std::string(name) + "'");
+  }
+  s.loaded = true;
+  return GR00T_OK;
+}
+
+int gr00t_finalize(gr00t_head* h) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (h->finalized) return GR00T_OK;
+  for (const std::string& n : h->order)
+    if (!h->specs[n].loaded) return fail(h, GR00T_E_MISSING_WEIGHT, "weight '" + n + "' was never loaded");
+  const gr00t_config& c = h->cfg;
+  HIPCHK(h, hipSetDevice(h->device));
+  if (hipMalloc((void**)&h->arena, h->lay.total) != hipSuccess) {
+    h->arena = nullptr;
+    (void)hipGetLastError();
+    return fail(h, GR00T_E_OOM, "hipMalloc of " + std::to_string(h->lay.total) + " weight bytes failed");
+  }
+  for (const std::string& n : h->order) {
+    Spec& s = h->specs[n];
+    size_t pos = 0;
+    for (const Piece& p : s.pieces) {
+      if (!s.matrix) {
+        HIPCHK(h, hipMemcpy(h->arena + p.off, s.staged.data(), s.staged.size(), hipMemcpyHostToDevice));
+        pos = s.staged.size();
+        continue;
+      }
+      const size_t nd = s.shape.size();
+      const size_t C = nd == 3 ? s.shape[0] : 1, OUT = s.shape[nd - 1];
+      const size_t esz = s.store == ST_F32 ? 4 : (s.store == ST_BF16 ? 2 : 1);
+      const size_t bytes = C * OUT * p.in_n * esz;
+      HIPCHK(h, hipMemcpy(h->arena + p.off, s.staged.data() + pos, bytes, hipMemcpyHostToDevice));
+      pos += bytes;
+      if (s.store == ST_FP8) {
+        HIPCHK(h, hipMemcpy(h->arena + p.scale_off, s.staged.data() + pos, C * OUT * 4, hipMemcpyHostToDevice));
+        pos += C * OUT * 4;
+      }
+    }
+    std::vector<uint8_t>().swap(s.staged);
+  }
+  // workspace
+  const size_t Bm = c.max_batch, Lm = c.max_vl_len, D = c.hidden, F = c.ff_dim, H = c.action_horizon, S = H + 1;
+  const size_t A = c.action_dim, E = c.vl_dim, K = c.num_steps, Nl = c.num_layers, Nc = (Nl + 1) / 2;
+  const size_t C = c.num_categories, T = c.time_freq_dim;
+  const size_t ab = act_bytes(h);
+  std::vector<std::pair<void**, size_t>> req = {
+      {(void**)&h->w.h, Bm * S * D * 4},      {&h->w.n, Bm * S * D * ab},       {&h->w.q, Bm * S * D * ab},
+      {&h->w.k, Bm * S * D * ab},             {&h->w.v, Bm * S * D * ab},       {&h->w.o, Bm * S * D * ab},
+      {&h->w.u, Bm * S * F * ab},             {&h->w.y, Bm * S * D * ab},       {&h->w.e1, Bm * H * D * ab},
+      {&h->w.e2, Bm * H * D * ab},            {&h->w.se1, Bm * D * ab},         {&h->w.vln, Bm * Lm * E * ab},
+      {&h->w.kc, Nc * Bm * Lm * D * ab},      {&h->w.vc, Nc * Bm * Lm * D * ab}, {(void**)&h->w.x, Bm * H * A * 4},
+      {(void**)&h->w.s, Bm * D * 4},          {(void**)&h->w.vout, Bm * H * A * 4},
+      {(void**)&h->w.code, Bm * Lm},          {(void**)&h->w.bad, Bm},           {(void**)&h->w.ids, Bm * 4},
+      {(void**)&h->w.iota, C * 4},            {(void**)&h->w.sin_t, K * T * 4},  {(void**)&h->w.t1, K * D * 4},
+      {(void**)&h->w.temb, K * D * 4},        {(void**)&h->w.stemb, K * D * 4},
+      {(void**)&h->w.ada, K * (Nl + 1) * 2 * D * 4},                              {(void**)&h->w.tauemb, K * D * 4},
+      {(void**)&h->w.c2tab, K * C * D * 4}};
+  size_t total = 0;
+  for (auto& r : req) total += (r.second + 255) & ~(size_t)255;
+  if (hipMalloc((void**)&h->wsbase, total) != hipSuccess) {
+    h->wsbase = nullptr;
+    (void)hipGetLastError();
+    return fail(h, GR00T_E_OOM, "hipMalloc of " + std::to_string(total) + " workspace bytes failed");
+  }
+  h->ws_bytes = total;
+  size_t off = 0;
+  for (auto& r : req) {
+    *r.first = h->wsbase + off;
+    off += (r.second + 255) & ~(size_t)255;
+  }
+  std::vector<int> iota(C);
+  for (size_t i = 0; i < C; ++i) iota[i] = (int)i;
+  HIPCHK(h, hipMemcpy(h->w.iota, iota.data(), C * 4, hipMemcpyHostToDevice));
+  HIPCHK(h, hipMemset(h->w.bad, 0, Bm));
+  HIPCHK(h, hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  HIPCHK(h, hipHostMalloc((void**)&h->bad_host, Bm, hipHostMallocDefault));
+  HIPCHK(h, hipEventCreateWithFlags(&h->bad_event, hipEventDisableTiming));
+  int rc = build_tables(h, h->cap_stream);
+  if (rc != GR00T_OK) return rc;
+  HIPCHK(h, hipStreamSynchronize(h->cap_stream));
+  h->finalized = true;
+  return GR00T_OK;
+}
+
+int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (!h->finalized) return fail(h, GR00T_E_NOT_FINALIZED, "handle is not finalized");
+  if (!(h->cfg.flags & GR00T_FLAG_USE_GRAPH)) return fail(h, GR00T_E_INVALID_ARG, "prepare needs GR00T_FLAG_USE_GRAPH");
+  if (batch < 1 || batch > h->cfg.max_batch || vl_len < 1 || vl_len > h->cfg.max_vl_len)
+    return fail(h, GR00T_E_SHAPE, "prepare shape outside capacity");
+  const auto key = std::make_pair((int)batch, (int)vl_len);
+  if (h->graphs.count(key)) return GR00T_OK;
+  HIPCHK(h, hipSetDevice(h->device));
+  hipGraph_t g = nullptr;
+  HIPCHK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  int rc = run_steps(h, batch, vl_len, 0, h->cfg.num_steps, true, h->cap_stream);
+  hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+  if (rc != GR00T_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(h, GR00T_E_HIP, std::string("hipStreamEndCapture failed: ") + hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(h, GR00T_E_HIP, std::string("hipGraphInstantiate failed: ") + hipGetErrorString(e));
+  h->graphs[key] = ex;
+  return GR00T_OK;
+}
+
+int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream) {
+  int rc = check_inputs(h, in, action_pred);
+  if (rc != GR00T_OK) return rc;
+  const bool use_graph = (h->cfg.flags & GR00T_FLAG_USE_GRAPH) != 0;
+  const auto key = std::make_pair((int)in->batch, (int)in->vl_len);
+  const bool have_graph = use_graph && h->graphs.count(key);
+  if (use_graph && !have_graph && (h->cfg.flags & GR00T_FLAG_STRICT))
+    return fail(h, GR00T_E_UNCAPTURED, "shape (B=" + std::to_string(in->batch) + ", L=" + std::to_string(in->vl_len) +
+                                           ") was not prepared");
+  hipStream_t s = (hipStream_t)hip_stream;
+  HIPCHK(h, hipSetDevice(h->device));
+  rc = pre_call_checks(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  rc = run_prologue(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  if (have_graph) {
+    HIPCHK(h, hipGraphLaunch(h->graphs[key], s));
+  } else {
+    rc = run_steps(h, in->batch, in->vl_len, 0, h->cfg.num_steps, true, s);
+    if (rc != GR00T_OK) return rc;
+  }
+  HIPCHK(h, launch_output(h->w.x, in->action_mask, h->w.bad, action_pred, in->batch,
+                          h->cfg.action_horizon * h->cfg.action_dim, s));
+  HIPCHK(h, hipMemcpyAsync(h->bad_host, h->w.bad, in->batch, hipMemcpyDeviceToHost, s));
+  HIPCHK(h, hipEventRecord(h->bad_event, s));
+  h->bad_pending_B = in->batch;
+  h->calls++;
+  return GR00T_OK;
+}
+
+int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v, void* hip_stream) {
+  int rc = check_inputs(h, in, v);
+  if (rc != GR00T_OK) return rc;
+  if (!in->noise) return fail(h, GR00T_E_INVALID_ARG, "gr00t_velocity needs inputs.noise");
+  if (step_k < 0 || step_k >= h->cfg.num_steps) return fail(h, GR00T_E_INVALID_ARG, "step_k outside [0, num_steps)");
+  hipStream_t s = (hipStream_t)hip_stream;
+  HIPCHK(h, hipSetDevice(h->device));
+  rc = pre_call_checks(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  rc = run_prologue(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  rc = run_steps(h, in->batch, in->vl_len, step_k, step_k + 1, false, s);
+  if (rc != GR00T_OK) return rc;
+  HIPCHK(h, hipMemcpyAsync(v, h->w.vout, sizeof(float) * in->batch * h->cfg.action_horizon * h->cfg.action_dim,
+                           hipMemcpyDeviceToDevice, s));
+  h->calls++;
+  return GR00T_OK;
+}
+
+void gr00t_destroy(gr00t_head* h) {
+  if (!h) return;
+  if (h->finalized || h->arena || h->wsbase) (void)hipSetDevice(h->device);
+  for (auto& kv : h->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (h->cap_stream) {
+    (void)hipStreamSynchronize(h->cap_stream);
+    (void)hipStreamDestroy(h->cap_stream);
+  }
+  if (h->bad_event) (void)hipEventDestroy(h->bad_event);
+  if (h->bad_host) (void)hipHostFree(h->bad_host);
+  if (h->arena || h->wsbase) (void)hipDeviceSynchronize();
+  if (h->arena) (void)hipFree(h->arena);
+  if (h->wsbase) (void)hipFree(h->wsbase);
+  delete h;
+}
+
+const char* gr00t_last_error(const gr00t_head* h) {
+  if (!h) return g_create_error.c_str();
+  return h->err.c_str();
+}
+
+size_t gr00t_device_bytes(const gr00t_head* h) {
+  if (!h || !h->finalized) return 0;
+  return h->lay.total + h->ws_bytes;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of the action head:
+// bf16 / e4m3 storage types, conversions, and wave64 reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gr00t {
+
+// bf16 storage: the upper 16 bits of an IEEE binary32 value.
+struct bf16 {
+  uint16_t u;
+};
+// OCP E4M3 ("fn") storage: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+struct fp8e4m3 {
+  uint8_t u;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN payloads are not preserved).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 0x7u;
+  if (e != 0) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
+  // subnormal: m * 2^-9, m = 1..7 (m = 0 gives +-0)
+  float v = (float)m * (1.0f / 512.0f);
+  return (uint16_t)(s | (__float_as_uint(v) >> 16));
+}
+
+__device__ __forceinline__ float e4m3_to_f(uint32_t c) { return bf16_to_f(e4m3_to_bf16(c)); }
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld<bf16>(const bf16* p) { return bf16_to_f(p->u); }
+template <>
+__device__ __forceinline__ float ld<fp8e4m3>(const fp8e4m3* p) { return e4m3_to_f(p->u); }
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, float v);
+template <>
+__device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void st<bf16>(bf16* p, float v) { p->u = f_to_bf16(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
+
+}  // namespace gr00t

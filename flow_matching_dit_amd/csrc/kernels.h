@@ -1,0 +1,112 @@
+// Launch interface of the gfx950 kernels of the GR00T action head.
+// Every launcher enqueues on the given stream and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gr00t {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum Act { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2, ACT_GELU = 3 };
+enum EpiKind {
+  EPI_STORE = 0,      // out[row, n] = act(v)            (fp32 or bf16 out)
+  EPI_RESID_ADD = 1,  // out[row, n] += act(v)           (fp32 residual stream)
+  EPI_HEADS = 2,      // scatter to head-major [b][head][pos][hd] buffers (act dtype)
+  EPI_EULER = 3       // out[row, n] += dt * act(v)      (fp32 Euler state)
+};
+
+// C[g, r, n] = sum_k A[g, r, k] * W[id_g][n, k]   (then * wscale[id_g][n] + bias[id_g][n])
+// A row (g, r) lives at A + (g * a_gstride + a_row_off + r) * lda.
+// W is packed [N][K] (K contiguous) per category; category = ids[g] (0 if ids == NULL).
+struct GemmArgs {
+  const void* A;
+  long lda;
+  long a_gstride;
+  int a_row_off;
+  const void* W;
+  long w_cstride;
+  const float* wscale;  // per-column fp32 scale of e4m3 weights, NULL otherwise
+  long s_cstride;
+  const float* bias;    // NULL = no bias
+  long b_cstride;
+  const int* ids;       // per-group category, NULL = category 0
+  int rows;             // rows per group
+  int N;
+  int K;
+  int groups;
+};
+
+struct Epi {
+  int kind;
+  int act;
+  void* out;
+  int out_f32;          // EPI_STORE: 1 = fp32 out, 0 = bf16 out
+  long out_ld;          // row stride of out (elements)
+  long out_gstride;     // rows between groups
+  int out_row_off;
+  const float* add_tab; // optional per-category row added before the activation
+  long add_cstride;
+  // EPI_HEADS: column n -> section sec = n / width, which = sec % nwhich,
+  // layer = sec / nwhich, head = (n % width) / hd, d = n % hd; row r -> (b, pos) with
+  // pos_per_b positions per sample; element goes to
+  // heads[which] + layer * layer_stride + ((b * nh + head) * pos_per_b + pos) * hd + d.
+  void* heads[3];
+  int nwhich;
+  int width;
+  int nh;
+  int hd;
+  int pos_per_b;
+  long layer_stride;
+  float dt;             // EPI_EULER
+};
+
+hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, const Epi& e, DType wt, hipStream_t s);
+
+// LayerNorm over rows of width D (eps 1e-5, population variance):
+//   y = (x - mean) / sqrt(var + eps) [* gamma + beta] [* (1 + scale) + shift]
+// with ada = [scale | shift] (2D floats) or NULL. x rows at x + r * ldx.
+hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt, long ldy, int rows,
+                            int D, const float* gamma, const float* beta, const float* ada,
+                            hipStream_t s);
+
+// Multi-head attention per (sample, head): softmax(q k^T / sqrt(hd)) v.
+// q [B][nh][S][hd], k/v [B][nh][Lk][hd] (act dtype); o [B*S][nh*hd] (act dtype).
+// mask: NULL = every key admitted; else key j of sample b is admitted iff
+// (mask[b * Lk + j] & mask_bit) != 0. A query with no admitted key outputs 0.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const uint8_t* mask;
+  int mask_bit;
+  int B, S, Lk, nh, hd;
+};
+hipError_t launch_attention(const AttnArgs& a, DType t, hipStream_t s);
+
+// Small kernels.
+// code[b*L + j] = bit0: admitted on text-attending blocks, bit1: on image-attending
+// blocks. Without an image mask both bits equal the valid bit.
+hipError_t launch_mask_codes(const uint8_t* vl_mask, const uint8_t* image_mask, uint8_t* code, int n,
+                             hipStream_t s);
+// ids_out[b] = ids_in[b] if in [0, C) else 0; bad[b] = out of range.
+hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C,
+                               hipStream_t s);
+// dst rows (b * dst_stride_rows + dst_row_off) <- src rows b (fp32, width D).
+hipError_t launch_copy_rows(const float* src, long src_ld, float* dst, long dst_ld, long dst_gstride,
+                            int dst_row_off, int B, int D, hipStream_t s);
+// x = noise (n floats), or N(0,1) from Philox4x32-10 + Box-Muller when noise == NULL.
+hipError_t launch_init_noise(const float* noise, float* x, long n, uint64_t seed, uint64_t counter,
+                             hipStream_t s);
+// out[b, i] = bad[b] ? NaN : x[b, i] * (mask ? mask[b, i] : 1), per = H*A.
+hipError_t launch_output(const float* x, const uint8_t* mask, const uint8_t* bad, float* out, int B,
+                         int per, hipStream_t s);
+// tab[k][i] = sinusoid(tau[k]) of width dim: [sin(tau w_i) | cos(tau w_i)], w_i = 10000^(-i/half).
+hipError_t launch_sinusoid(const int* tau_host_k, int K, int dim, float* tab, hipStream_t s);
+// y = SiLU(x), n floats.
+hipError_t launch_silu(const float* x, float* y, long n, hipStream_t s);
+// fp32 -> act dtype copy of n elements.
+hipError_t launch_convert(const float* x, void* y, DType yt, long n, hipStream_t s);
+
+}  // namespace gr00t

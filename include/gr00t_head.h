@@ -1,0 +1,181 @@
+/*
+ * gr00t_head.h -- C ABI of the MI355X (gfx950) GR00T flow-matching DiT action head.
+ *
+ * The head is System 1 of the GR00T vision-language-action model ("Model
+ * architecture" page, sections "Action head architecture", "Diffusion
+ * transformer (DiT)", "AlternateVLDiT variant", "Flow matching diffusion" and
+ * "Embodiment-specific projectors"; "GR00T model class" page, section
+ * "get_action"). Given backbone features [B, L, 2048] with their attention and
+ * image masks, the robot state and an embodiment id per sample, it integrates
+ * K Euler steps  x <- x + (1/K) * v(x, tau_k)  of a DiT velocity field starting
+ * from Gaussian noise and returns action_pred [B, H, A].
+ *
+ * Conventions for every entry point:
+ *   - Return value: GR00T_OK (0) or a negative gr00t_status. No C++ exception
+ *     crosses this boundary. The message of the last failure on a handle is
+ *     returned by gr00t_last_error(handle).
+ *   - Every argument check runs before any device work is enqueued.
+ *   - "device" pointers point to memory on the handle's GPU; "host" pointers to
+ *     ordinary host memory. The caller owns every buffer it passes and keeps it
+ *     valid until the work on the given stream has completed.
+ *   - One call may be in flight per handle at a time; distinct handles are
+ *     independent.
+ */
+#ifndef GR00T_HEAD_H
+#define GR00T_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gr00t_status {
+  GR00T_OK = 0,
+  GR00T_E_INVALID_ARG = -1,    /* NULL handle/pointer, bad enum, inconsistent config */
+  GR00T_E_SHAPE = -2,          /* B > max_batch, L_pad > max_vl_len, weight shape mismatch */
+  GR00T_E_EMBODIMENT = -3,     /* strict mode: an embodiment id outside [0, num_categories) */
+  GR00T_E_NOT_FINALIZED = -4,  /* get_action/prepare before finalize, or load after it */
+  GR00T_E_UNKNOWN_WEIGHT = -5, /* load_weights with a name the config does not define */
+  GR00T_E_UNCAPTURED = -6,     /* USE_GRAPH|STRICT and (B, L_pad) was not prepared */
+  GR00T_E_HIP = -7,            /* a HIP runtime call failed (message names it) */
+  GR00T_E_OOM = -8,            /* device allocation failed */
+  GR00T_E_MISSING_WEIGHT = -9, /* finalize with a weight never loaded */
+  GR00T_E_DEVICE_ERROR = -10   /* a previous call met an invalid id in non-strict mode */
+} gr00t_status;
+
+typedef enum gr00t_dtype {
+  GR00T_F32 = 0,
+  GR00T_BF16 = 1,
+  GR00T_FP8_E4M3 = 2, /* OCP E4M3 ("fn": no inf, max 448) */
+  GR00T_U8 = 3,
+  GR00T_I32 = 4
+} gr00t_dtype;
+
+/* Flags of gr00t_config.flags. */
+#define GR00T_FLAG_STRICT 0x1u    /* validate ids on the host (one device->host copy) and
+                                     refuse unprepared shapes in graph mode */
+#define GR00T_FLAG_USE_GRAPH 0x2u /* replay the K-step loop from a captured hipGraph */
+
+/*
+ * Model and capacity. Widths follow the "Model configuration" table of the
+ * architecture page: hidden = num_heads * head_dim is used for the state and
+ * action encoders' output, the DiT inner width and the decoder's hidden width.
+ */
+typedef struct gr00t_config {
+  int32_t num_layers;        /* DiT blocks; even index = cross-attention, odd = self */
+  int32_t hidden;            /* D */
+  int32_t num_heads;
+  int32_t head_dim;          /* D == num_heads * head_dim; head_dim <= 64, multiple of 16 */
+  int32_t ff_dim;            /* F, GELU MLP width */
+  int32_t vl_dim;            /* backbone_embedding_dim (2048 on the pages) */
+  int32_t state_dim;         /* state features per sample (one state token) */
+  int32_t action_dim;        /* A */
+  int32_t action_horizon;    /* H; the DiT sees S = 1 + H tokens */
+  int32_t num_categories;    /* C, embodiment tables */
+  int32_t num_steps;         /* K Euler steps (num_inference_timesteps) */
+  int32_t num_timestep_buckets;       /* 1000 */
+  int32_t attend_text_every_n_blocks; /* n of the AlternateVLDiT text/image alternation */
+  int32_t time_freq_dim;     /* width of the timestep sinusoid fed to the timestep encoder */
+  int32_t max_batch;         /* capacity: largest B served */
+  int32_t max_vl_len;        /* capacity: largest L_pad served */
+  gr00t_dtype weight_dtype;  /* F32, BF16 or FP8_E4M3 (e4m3 DiT matrices, the rest bf16) */
+  gr00t_dtype act_dtype;     /* F32 (with F32 weights) or BF16 */
+  uint32_t flags;            /* GR00T_FLAG_* */
+  uint64_t noise_seed;       /* seed of the library's N(0,1) draw when inputs.noise == NULL */
+} gr00t_config;
+
+/*
+ * Inputs of one get_action call ("GR00T model class", get_action; the backbone
+ * output dict of the architecture page: backbone_features, backbone_attention_mask,
+ * image_mask). All pointers are device pointers unless noted.
+ */
+typedef struct gr00t_inputs {
+  int32_t batch;                 /* B (host value), 1 <= B <= max_batch */
+  int32_t vl_len;                /* L_pad (host value), 1 <= L_pad <= max_vl_len */
+  const void* vl_features;       /* [B, L_pad, vl_dim] in act_dtype, row-major */
+  const uint8_t* vl_mask;        /* [B, L_pad] 0/1, NULL = every position valid */
+  const uint8_t* image_mask;     /* [B, L_pad] 0/1, NULL = no image/text split: every
+                                    cross block attends to all valid positions */
+  const float* state;            /* [B, 1, state_dim] f32 */
+  const int32_t* embodiment_id;  /* [B] in [0, num_categories) */
+  const float* noise;            /* [B, H, A] f32 initial Euler state; NULL = drawn by
+                                    the library from N(0,1) with noise_seed and a call
+                                    counter (not reproducible across handles) */
+  const uint8_t* action_mask;    /* [B, H, A] 0/1 applied to the final chunk; NULL = ones */
+  float* state_features_out;     /* optional [B, 1, hidden] f32 output; NULL = not written */
+} gr00t_inputs;
+
+typedef struct gr00t_head gr00t_head;
+
+/* Create a handle for device `device`. Checks the config only; no device memory
+ * is allocated until gr00t_finalize. *out is set to NULL on failure. */
+int gr00t_create(const gr00t_config* cfg, int device, gr00t_head** out);
+
+/*
+ * Copy one parameter tensor from host memory (the caller may free it on return).
+ * `name` is one of the canonical names below, `dtype` is GR00T_F32 (fp32 masters:
+ * the library rounds to bf16 with round-to-nearest-even, or quantises DiT matrices
+ * to e4m3 with one fp32 scale per output column, scale = max|W[:,o]| / 448) or
+ * GR00T_BF16 (raw bf16 bits; not for fp8 matrices). `shape` must equal the
+ * canonical shape. Every linear is stored [in, out] (y = x @ W + b), with a leading
+ * category axis C for per-embodiment tables:
+ *   vlln.gamma [E]  vlln.beta [E]                       (E = vl_dim)
+ *   time.w1 [T, D]  time.b1 [D]  time.w2 [D, D]  time.b2 [D]     (T = time_freq_dim)
+ *   state_enc.w1 [C, Sd, D]  .b1 [C, D]  .w2 [C, D, D]  .b2 [C, D]
+ *   action_enc.w1 [C, A, D] .b1 [C, D] .w2 [C, 2D, D] .b2 [C, D] .w3 [C, D, D] .b3 [C, D]
+ *   blocks.{l}.ada.w [D, 2D]  .ada.b [2D]
+ *   blocks.{l}.attn.wq [D, D] .bq [D] .wk [Din, D] .bk [D] .wv [Din, D] .bv [D]
+ *                  .wo [D, D] .bo [D]      (Din = E for even l, D for odd l)
+ *   blocks.{l}.ff.w1 [D, F]  .b1 [F]  .w2 [F, D]  .b2 [D]
+ *   out.ada.w [D, 2D]  out.ada.b [2D]  out.proj.w [D, D]  out.proj.b [D]
+ *   action_dec.w1 [C, D, D]  .b1 [C, D]  .w2 [C, D, A]  .b2 [C, A]
+ * Errors: E_UNKNOWN_WEIGHT, E_SHAPE, E_INVALID_ARG (dtype), E_NOT_FINALIZED (after
+ * finalize). Loading a name twice replaces it. Host-only; no device work.
+ */
+int gr00t_load_weights(gr00t_head* h, const char* name, const void* host_data,
+                       gr00t_dtype dtype, const int64_t* shape, int ndim);
+
+/* Check that every weight was loaded (E_MISSING_WEIGHT names the first missing
+ * one), upload and pack them, allocate the workspace for (max_batch, max_vl_len)
+ * and compute the input-independent per-step tables (timestep embedding, adaLN
+ * scale/shift of every block and of the output norm, the timestep half of the
+ * action encoder's second linear). Synchronous. */
+int gr00t_finalize(gr00t_head* h);
+
+/* Capture the K-step hipGraph for batch B and padded VL length L_pad (the analogue
+ * of capture profiles). Needs GR00T_FLAG_USE_GRAPH; synchronous. */
+int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len);
+
+/*
+ * One get_action call: action_pred [B, H, A] f32 (device) = the masked chunk after
+ * K Euler steps. Enqueued on `hip_stream` (a hipStream_t; NULL = default stream) and
+ * returns without waiting, except in strict mode where the ids are first copied to
+ * the host and checked (E_EMBODIMENT). In non-strict mode an out-of-range id is
+ * not read: its sample's rows of action_pred are NaN, and the next call on the
+ * handle returns E_DEVICE_ERROR once.
+ */
+int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
+                     void* hip_stream);
+
+/* Debug and test entry: the velocity v(x = noise, tau_k) of Euler step `step_k`
+ * ([B, H, A] f32, device), without integration or action_mask. inputs.noise must
+ * not be NULL. Same stream semantics as gr00t_get_action. */
+int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v,
+                   void* hip_stream);
+
+/* Release graphs, device weights and workspace. NULL is a no-op. */
+void gr00t_destroy(gr00t_head* h);
+
+/* Message of the last failure on `h` ("" if none); with h == NULL, the last failure
+ * of gr00t_create in this thread. The pointer stays valid until the next call on h. */
+const char* gr00t_last_error(const gr00t_head* h);
+
+/* Bytes of device memory held by the handle after finalize (weights + workspace). */
+size_t gr00t_device_bytes(const gr00t_head* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GR00T_HEAD_H */

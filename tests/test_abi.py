@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before any device work (gr00t_create and
+gr00t_load_weights touch no device; the other entry points validate first)."""
+import ctypes
+import os
+import re
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from flow_matching_dit_amd import head as H
+from flow_matching_dit_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _cfg(**kw):
+    return replace(synth.TINY, **kw)
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "gr00t_head.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gr00t_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = H.load_library()
+    declared = _header_functions()
+    assert set(declared) == set(H.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header():
+    # gr00t_config: 16 int32 + 2 enums + uint32 flags + uint64 seed (8-aligned)
+    assert ctypes.sizeof(H.Gr00tConfig) == 16 * 4 + 2 * 4 + 4 + 4 + 8
+    assert H.Gr00tConfig.noise_seed.offset == 80
+    # gr00t_inputs: two int32 then eight pointers
+    assert ctypes.sizeof(H.Gr00tInputs) == 8 + 8 * 8
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(hidden=250), "hidden must equal"),
+    (dict(head_dim=80, hidden=320, num_heads=4), "head_dim"),
+    (dict(num_steps=0), "num_steps"),
+    (dict(action_horizon=65), "action_horizon"),
+    (dict(precision="bf16"), None),
+])
+def test_create_validates_config(kw, frag):
+    if frag is None:
+        h = H.Gr00tHead(_cfg(**kw), max_batch=2, max_vl_len=8)
+        h.close()
+        return
+    with pytest.raises(H.Gr00tError) as e:
+        H.Gr00tHead(_cfg(**kw), max_batch=2, max_vl_len=8)
+    assert e.value.status == "E_INVALID_ARG" and frag in str(e.value)
+
+
+def test_create_rejects_mixed_precisions_and_capacity():
+    lib = H.load_library()
+    c = H.make_config(synth.TINY, 1, 8)
+    c.act_dtype = H.BF16
+    out = ctypes.c_void_p()
+    assert lib.gr00t_create(ctypes.byref(c), 0, ctypes.byref(out)) == -1
+    assert b"F32 weights" in lib.gr00t_last_error(None)
+    assert out.value is None
+    c = H.make_config(synth.TINY, 0, 8)
+    assert lib.gr00t_create(ctypes.byref(c), 0, ctypes.byref(out)) == -1
+    assert lib.gr00t_create(None, 0, ctypes.byref(out)) == -1
+
+
+def test_load_weights_errors():
+    w = synth.WORKLOADS["tiny_fp32_b1"]
+    h = H.Gr00tHead(w.cfg, max_batch=1, max_vl_len=32)
+    with pytest.raises(H.Gr00tError) as e:
+        h.load_weight("blocks.9.attn.wq", np.zeros((256, 256), np.float32))
+    assert e.value.status == "E_UNKNOWN_WEIGHT"
+    with pytest.raises(H.Gr00tError) as e:
+        h.load_weight("blocks.0.attn.wk", np.zeros((256, 256), np.float32))  # cross block: [2048, 256]
+    assert e.value.status == "E_SHAPE" and "[2048,256]" in str(e.value)
+    with pytest.raises(H.Gr00tError) as e:
+        h.load_weight("time.w1", np.zeros((256, 256), np.uint16), dtype=H.BF16)  # fp32 handle
+    assert e.value.status == "E_INVALID_ARG"
+    with pytest.raises(H.Gr00tError) as e:
+        h.load_weight("vlln.gamma", np.zeros((2048,), np.float32), dtype=7)
+    assert e.value.status == "E_INVALID_ARG"
+    h.close()
+
+
+def test_finalize_reports_missing_weight_without_device():
+    w = synth.WORKLOADS["tiny_fp32_b1"]
+    h = H.Gr00tHead(w.cfg, max_batch=1, max_vl_len=32)
+    weights = synth.make_weights(w)
+    for name in list(weights)[:-1]:
+        h.load_weight(name, weights[name])
+    with pytest.raises(H.Gr00tError) as e:
+        h.finalize()
+    assert e.value.status == "E_MISSING_WEIGHT" and "action_dec.b2" in str(e.value)
+    h.close()
+
+
+def test_fp8_matrices_refuse_raw_bf16():
+    cfg = _cfg(precision="fp8")
+    h = H.Gr00tHead(cfg, max_batch=1, max_vl_len=8)
+    with pytest.raises(H.Gr00tError) as e:
+        h.load_weight("blocks.1.attn.wq", np.zeros((256, 256), np.uint16), dtype=H.BF16)
+    assert e.value.status == "E_INVALID_ARG"
+    h.load_weight("blocks.1.ada.w", np.zeros((256, 512), np.uint16), dtype=H.BF16)  # bf16 matrix: accepted
+    h.close()
+
+
+def _fake_inputs(B, L):
+    p = ctypes.c_void_p(0x1000)
+    return H.Gr00tInputs(B, L, p, None, None, p, p, None, None, None)
+
+
+def test_get_action_validates_before_device_work():
+    lib = H.load_library()
+    h = H.Gr00tHead(synth.TINY, max_batch=2, max_vl_len=32)
+    out = ctypes.c_void_p(0x2000)
+    cases = [(_fake_inputs(3, 8), -2, b"batch 3"), (_fake_inputs(1, 33), -2, b"vl_len 33"),
+             (_fake_inputs(0, 8), -2, b"batch 0"), (_fake_inputs(1, 8), -4, b"not finalized")]
+    for inp, code, msg in cases:
+        assert lib.gr00t_get_action(h.h, ctypes.byref(inp), out, None) == code
+        assert msg in lib.gr00t_last_error(h.h)
+    bad = _fake_inputs(1, 8)
+    bad.state = None
+    assert lib.gr00t_get_action(h.h, ctypes.byref(bad), out, None) == -1
+    assert lib.gr00t_get_action(h.h, None, out, None) == -1
+    assert lib.gr00t_get_action(h.h, ctypes.byref(_fake_inputs(1, 8)), None, None) == -1
+    assert lib.gr00t_get_action(None, ctypes.byref(_fake_inputs(1, 8)), out, None) == -1
+    nz = _fake_inputs(1, 8)
+    assert lib.gr00t_velocity(h.h, ctypes.byref(nz), 0, out, None) == -4
+    assert lib.gr00t_prepare(h.h, 1, 8) == -4
+    assert lib.gr00t_device_bytes(h.h) == 0
+    h.close()
+
+
+def test_destroy_null_and_last_error_null():
+    lib = H.load_library()
+    lib.gr00t_destroy(None)
+    assert isinstance(lib.gr00t_last_error(None), bytes)
+
+
+def test_canonical_weight_names_are_accepted():
+    w = synth.small_variant(synth.WORKLOADS["dit32_bf16_b64"], num_layers=3)
+    h = H.Gr00tHead(w.cfg, max_batch=2, max_vl_len=16)
+    for name, shape in synth.weight_shapes(w.cfg).items():
+        h.load_weight(name, np.zeros(shape, np.float32))
+    h.close()

@@ -14,12 +14,15 @@
 // The K-step part can be captured once per (B, L_pad) into a hipGraph.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <map>
 #include <new>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -140,6 +143,13 @@ struct gr00t_head {
   hipEvent_t bad_event = nullptr;
   int bad_pending_B = 0;
   std::vector<int> tau;
+  // launch timing (gr00t_profile_*)
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_pool;
+  std::vector<std::pair<int, int>> prof_recs;  // (class, index of the start event)
+  size_t prof_next = 0;
+  std::vector<int64_t> prof_n;
+  std::vector<double> prof_ms;
 };
 
 namespace {
@@ -317,12 +327,30 @@ void build_specs(gr00t_head* h) {
   L.total = off;
 }
 
-// Pack a loaded tensor (fp32 values or raw bf16 bits) into its pieces.
+// Run f(i) for i in [0, n) on up to hardware_concurrency threads.
+template <typename Fn>
+void parallel_for(int64_t n, Fn f) {
+  unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (n < 2 || nt == 1) {
+    for (int64_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::atomic<int64_t> next{0};
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([&]() {
+      for (int64_t i = next.fetch_add(1); i < n; i = next.fetch_add(1)) f(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+// Pack a loaded tensor (fp32 values or raw bf16 bits) into its pieces. Matrices
+// [C][IN][OUT] become [C][OUT][in_n] (the slice [in_lo, in_lo + in_n) of IN), in
+// 64 x 64 blocks so both sides are read and written in cache lines.
 void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
-  auto val = [&](size_t i) -> float {
-    if (dt == GR00T_F32) return ((const float*)data)[i];
-    return host_bf16_to_f32(((const uint16_t*)data)[i]);
-  };
+  const float* f32 = (const float*)data;
+  const uint16_t* b16 = (const uint16_t*)data;
+  auto val = [&](size_t i) -> float { return dt == GR00T_F32 ? f32[i] : host_bf16_to_f32(b16[i]); };
   size_t numel = 1;
   for (auto d : s.shape) numel *= (size_t)d;
   s.staged.clear();
@@ -335,38 +363,45 @@ void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
   }
   const size_t nd = s.shape.size();
   const int64_t C = nd == 3 ? s.shape[0] : 1, IN = s.shape[nd - 2], OUT = s.shape[nd - 1];
+  constexpr int64_t BLK = 64;
   for (const Piece& p : s.pieces) {
     const int64_t in_n = p.in_n;
     const size_t base = s.staged.size();
-    if (s.store == ST_F32) {
-      s.staged.resize(base + (size_t)C * OUT * in_n * 4);
-      float* o = (float*)(s.staged.data() + base);
-      for (int64_t cc = 0; cc < C; ++cc)
-        for (int64_t oo = 0; oo < OUT; ++oo)
-          for (int64_t i = 0; i < in_n; ++i) o[(cc * OUT + oo) * in_n + i] = val((cc * IN + p.in_lo + i) * OUT + oo);
-    } else if (s.store == ST_BF16) {
-      s.staged.resize(base + (size_t)C * OUT * in_n * 2);
-      uint16_t* o = (uint16_t*)(s.staged.data() + base);
-      for (int64_t cc = 0; cc < C; ++cc)
-        for (int64_t oo = 0; oo < OUT; ++oo)
-          for (int64_t i = 0; i < in_n; ++i)
-            o[(cc * OUT + oo) * in_n + i] = dt == GR00T_BF16
-                                                ? ((const uint16_t*)data)[(cc * IN + p.in_lo + i) * OUT + oo]
-                                                : host_f32_to_bf16(val((cc * IN + p.in_lo + i) * OUT + oo));
-    } else {  // e4m3 with one fp32 scale per output column: codes then scales
-      s.staged.resize(base + (size_t)C * OUT * in_n + (size_t)C * OUT * 4);
-      uint8_t* o = s.staged.data() + base;
-      float* sc = (float*)(s.staged.data() + base + (size_t)C * OUT * in_n);
-      for (int64_t cc = 0; cc < C; ++cc)
-        for (int64_t oo = 0; oo < OUT; ++oo) {
-          float amax = 0.0f;
-          for (int64_t i = 0; i < in_n; ++i) amax = std::fmax(amax, std::fabs(val((cc * IN + p.in_lo + i) * OUT + oo)));
-          const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-          sc[cc * OUT + oo] = scale;
-          for (int64_t i = 0; i < in_n; ++i)
-            o[(cc * OUT + oo) * in_n + i] = host_f32_to_e4m3(val((cc * IN + p.in_lo + i) * OUT + oo) / scale);
+    const size_t esz = s.store == ST_F32 ? 4 : (s.store == ST_BF16 ? 2 : 1);
+    const size_t nbytes = (size_t)C * OUT * in_n * esz + (s.store == ST_FP8 ? (size_t)C * OUT * 4 : 0);
+    s.staged.resize(base + nbytes);
+    uint8_t* dst = s.staged.data() + base;
+    float* scales = (float*)(dst + (size_t)C * OUT * in_n);
+    if (s.store == ST_FP8) {  // per-column scale = max |W[:, o]| / 448 (1 for an all-zero column)
+      parallel_for(C, [&](int64_t cc) {
+        std::vector<float> amax(OUT, 0.0f);
+        for (int64_t i = 0; i < in_n; ++i) {
+          const size_t row = (size_t)(cc * IN + p.in_lo + i) * OUT;
+          for (int64_t oo = 0; oo < OUT; ++oo) amax[oo] = std::fmax(amax[oo], std::fabs(val(row + oo)));
         }
+        for (int64_t oo = 0; oo < OUT; ++oo) scales[cc * OUT + oo] = amax[oo] > 0.0f ? amax[oo] / 448.0f : 1.0f;
+      });
     }
+    const int64_t nob = (OUT + BLK - 1) / BLK;
+    parallel_for(C * nob, [&](int64_t task) {
+      const int64_t cc = task / nob, o0 = (task % nob) * BLK, o1 = std::min(OUT, o0 + BLK);
+      for (int64_t i0 = 0; i0 < in_n; i0 += BLK) {
+        const int64_t i1 = std::min(in_n, i0 + BLK);
+        for (int64_t oo = o0; oo < o1; ++oo) {
+          const size_t drow = (size_t)(cc * OUT + oo) * in_n;
+          for (int64_t i = i0; i < i1; ++i) {
+            const size_t si = (size_t)(cc * IN + p.in_lo + i) * OUT + oo;
+            if (s.store == ST_F32) {
+              ((float*)dst)[drow + i] = val(si);
+            } else if (s.store == ST_BF16) {
+              ((uint16_t*)dst)[drow + i] = dt == GR00T_BF16 ? b16[si] : host_f32_to_bf16(val(si));
+            } else {
+              dst[drow + i] = host_f32_to_e4m3(val(si) / scales[cc * OUT + oo]);
+            }
+          }
+        }
+      }
+    });
   }
 }
 
@@ -375,6 +410,55 @@ void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
     hipError_t e__ = (expr);                                                                              \
     if (e__ != hipSuccess)                                                                                \
       return fail((h), GR00T_E_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e__));           \
+  } while (0)
+
+// ------------------------------------------------------------------ launch timing
+
+enum KClass {
+  K_VLLN = 0, K_KV_PROJ, K_STATE_ENC, K_ACTION_ENC, K_ADALN, K_QKV_PROJ, K_Q_PROJ, K_ATTN_SELF, K_ATTN_CROSS,
+  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_NCLASS
+};
+const char* const kClassNames[K_NCLASS] = {"vlln", "kv_proj", "state_enc", "action_enc", "adaln", "qkv_proj",
+                                           "q_proj", "attn_self", "attn_cross", "o_proj", "norm3", "ff_up",
+                                           "ff_down", "out_proj", "decoder", "small"};
+
+// Returns the index of the start event recorded on s, or -1 when not profiling.
+int prof_begin(gr00t_head* h, hipStream_t s) {
+  if (!h->prof_on) return -1;
+  while (h->prof_pool.size() < h->prof_next + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    h->prof_pool.push_back(e);
+  }
+  const int i = (int)h->prof_next;
+  h->prof_next += 2;
+  if (hipEventRecord(h->prof_pool[i], s) != hipSuccess) return -1;
+  return i;
+}
+
+void prof_end(gr00t_head* h, hipStream_t s, int cls, int i) {
+  if (i < 0) return;
+  if (hipEventRecord(h->prof_pool[i + 1], s) == hipSuccess) h->prof_recs.emplace_back(cls, i);
+}
+
+int prof_collect(gr00t_head* h) {
+  for (const auto& r : h->prof_recs) {
+    HIPCHK(h, hipEventSynchronize(h->prof_pool[r.second + 1]));
+    float ms = 0.0f;
+    HIPCHK(h, hipEventElapsedTime(&ms, h->prof_pool[r.second], h->prof_pool[r.second + 1]));
+    h->prof_n[r.first] += 1;
+    h->prof_ms[r.first] += ms;
+  }
+  h->prof_recs.clear();
+  h->prof_next = 0;
+  return GR00T_OK;
+}
+
+#define LAUNCH(h, s, cls, expr)          \
+  do {                                   \
+    const int ev__ = prof_begin((h), (s)); \
+    HIPCHK((h), (expr));                 \
+    prof_end((h), (s), (cls), ev__);     \
   } while (0)
 
 template <typename T>
@@ -476,9 +560,9 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
   const DType A = h->act;
   const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
   const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
-  HIPCHK(h, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
-  HIPCHK(h, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
-  HIPCHK(h, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
+  LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
+  LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
+  LAUNCH(h, s, K_VLLN, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
                              at<float>(h, lay.vlln_b), nullptr, s));
   {  // keys and values of every cross block: [B*L, E] x [Nc*2D, E]^T -> head-major caches
     GemmArgs a = ga(h->w.vln, E, B * L, Nc * 2 * D, E);
@@ -496,7 +580,7 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     e.hd = c.head_dim;
     e.pos_per_b = L;
     e.layer_stride = (long)B * L * D;
-    HIPCHK(h, gemm(h, a, e, A, kvw, s));
+    LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));
   }
   {  // state encoder: one token per sample
     GemmArgs a = ga(in->state, c.state_dim, 1, D, c.state_dim);
@@ -509,7 +593,7 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     a.b_cstride = D;
     Epi e = ep_store(h->w.se1, A == DT_F32, D, ACT_RELU);
     e.out_gstride = 1;
-    HIPCHK(h, gemm(h, a, e, DT_F32, mw, s));
+    LAUNCH(h, s, K_STATE_ENC, gemm(h, a, e, DT_F32, mw, s));
     a = ga(h->w.se1, D, 1, D, D);
     a.groups = B;
     a.a_gstride = 1;
@@ -520,12 +604,12 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     a.b_cstride = D;
     e = ep_store(h->w.s, true, D);
     e.out_gstride = 1;
-    HIPCHK(h, gemm(h, a, e, A, mw, s));
+    LAUNCH(h, s, K_STATE_ENC, gemm(h, a, e, A, mw, s));
     if (in->state_features_out)
-      HIPCHK(h, launch_copy_rows(h->w.s, D, in->state_features_out, D, 1, 0, B, D, s));
+      LAUNCH(h, s, K_SMALL, launch_copy_rows(h->w.s, D, in->state_features_out, D, 1, 0, B, D, s));
   }
   const long nx = (long)B * c.action_horizon * c.action_dim;
-  HIPCHK(h, launch_init_noise(in->noise, h->w.x, nx, c.noise_seed, h->calls, s));
+  LAUNCH(h, s, K_SMALL, launch_init_noise(in->noise, h->w.x, nx, c.noise_seed, h->calls, s));
   return GR00T_OK;
 }
 
@@ -555,7 +639,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       a.b_cstride = D;
       Epi e = ep_store(h->w.e1, f32, D);
       e.out_gstride = H;
-      HIPCHK(h, gemm(h, a, e, DT_F32, mw, s));
+      LAUNCH(h, s, K_ACTION_ENC, gemm(h, a, e, DT_F32, mw, s));
       a = ga(h->w.e1, D, H, D, D);
       a.groups = B;
       a.a_gstride = H;
@@ -566,7 +650,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       e.out_gstride = H;
       e.add_tab = h->w.c2tab + (size_t)k * c.num_categories * D;
       e.add_cstride = D;
-      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      LAUNCH(h, s, K_ACTION_ENC, gemm(h, a, e, A, mw, s));
       a = ga(h->w.e2, D, H, D, D);
       a.groups = B;
       a.a_gstride = H;
@@ -578,15 +662,15 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       e = ep_store(h->w.h, true, D);
       e.out_gstride = S;
       e.out_row_off = 1;
-      HIPCHK(h, gemm(h, a, e, A, mw, s));
-      HIPCHK(h, launch_copy_rows(h->w.s, D, h->w.h, D, S, 0, B, D, s));
+      LAUNCH(h, s, K_ACTION_ENC, gemm(h, a, e, A, mw, s));
+      LAUNCH(h, s, K_SMALL, launch_copy_rows(h->w.s, D, h->w.h, D, S, 0, B, D, s));
     }
     // ---- DiT blocks
     for (int l = 0; l < Nl; ++l) {
       const LayerOff& lo = lay.L[l];
       const bool self = (l % 2) == 1;
       const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + l) * 2 * D;
-      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
       {
         GemmArgs a = ga(h->w.n, D, (int)M, (self ? 3 : 1) * D, D);
         a.W = at<void>(h, lo.wq);
@@ -604,7 +688,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         e.hd = hd;
         e.pos_per_b = S;
         e.layer_stride = 0;
-        HIPCHK(h, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, self ? K_QKV_PROJ : K_Q_PROJ, gemm(h, a, e, A, dw, s));
       }
       AttnArgs at_{};
       at_.q = h->w.q;
@@ -626,7 +710,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         at_.mask = h->w.code;
         at_.mask_bit = (l % (2 * c.attend_text_every_n_blocks) == 0) ? 1 : 2;
       }
-      HIPCHK(h, launch_attention(at_, A, s));
+      LAUNCH(h, s, self ? K_ATTN_SELF : K_ATTN_CROSS, launch_attention(at_, A, s));
       {
         GemmArgs a = ga(h->w.o, D, (int)M, D, D);
         a.W = at<void>(h, lo.wo);
@@ -634,33 +718,33 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.so) : nullptr;
         Epi e = ep_store(h->w.h, true, D);
         e.kind = EPI_RESID_ADD;
-        HIPCHK(h, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, K_O_PROJ, gemm(h, a, e, A, dw, s));
       }
-      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, nullptr, s));
+      LAUNCH(h, s, K_NORM3, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, nullptr, s));
       {
         GemmArgs a = ga(h->w.n, D, (int)M, F, D);
         a.W = at<void>(h, lo.w1);
         a.bias = at<float>(h, lo.b1);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.s1) : nullptr;
-        HIPCHK(h, gemm(h, a, ep_store(h->w.u, f32, F, ACT_GELU), A, dw, s));
+        LAUNCH(h, s, K_FF_UP, gemm(h, a, ep_store(h->w.u, f32, F, ACT_GELU), A, dw, s));
         a = ga(h->w.u, F, (int)M, D, F);
         a.W = at<void>(h, lo.w2);
         a.bias = at<float>(h, lo.b2);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.s2) : nullptr;
         Epi e = ep_store(h->w.h, true, D);
         e.kind = EPI_RESID_ADD;
-        HIPCHK(h, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, K_FF_DOWN, gemm(h, a, e, A, dw, s));
       }
     }
     // ---- output adaLN + projection, then decoder and Euler update
     {
       const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + Nl) * 2 * D;
-      HIPCHK(h, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
       GemmArgs a = ga(h->w.n, D, (int)M, D, D);
       a.W = at<void>(h, lay.p_w);
       a.bias = at<float>(h, lay.p_b);
       a.wscale = dw == DT_FP8 ? at<float>(h, lay.p_s) : nullptr;
-      HIPCHK(h, gemm(h, a, ep_store(h->w.y, f32, D), A, dw, s));
+      LAUNCH(h, s, K_OUT_PROJ, gemm(h, a, ep_store(h->w.y, f32, D), A, dw, s));
       a = ga(h->w.y, D, H, D, D);
       a.groups = B;
       a.a_gstride = S;
@@ -672,7 +756,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       a.b_cstride = D;
       Epi e = ep_store(h->w.e1, f32, D, ACT_RELU);
       e.out_gstride = H;
-      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      LAUNCH(h, s, K_DECODER, gemm(h, a, e, A, mw, s));
       a = ga(h->w.e1, D, H, Adim, D);
       a.groups = B;
       a.a_gstride = H;
@@ -689,7 +773,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         e = ep_store(h->w.vout, true, Adim);
       }
       e.out_gstride = H;
-      HIPCHK(h, gemm(h, a, e, A, mw, s));
+      LAUNCH(h, s, K_DECODER, gemm(h, a, e, A, mw, s));
     }
   }
   return GR00T_OK;
@@ -886,7 +970,10 @@ int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len) {
   HIPCHK(h, hipSetDevice(h->device));
   hipGraph_t g = nullptr;
   HIPCHK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  const bool prof = h->prof_on;
+  h->prof_on = false;  // no event records inside the graph
   int rc = run_steps(h, batch, vl_len, 0, h->cfg.num_steps, true, h->cap_stream);
+  h->prof_on = prof;
   hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
   if (rc != GR00T_OK) {
     if (g) (void)hipGraphDestroy(g);
@@ -906,7 +993,7 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
   if (rc != GR00T_OK) return rc;
   const bool use_graph = (h->cfg.flags & GR00T_FLAG_USE_GRAPH) != 0;
   const auto key = std::make_pair((int)in->batch, (int)in->vl_len);
-  const bool have_graph = use_graph && h->graphs.count(key);
+  const bool have_graph = use_graph && h->graphs.count(key) && !h->prof_on;
   if (use_graph && !have_graph && (h->cfg.flags & GR00T_FLAG_STRICT))
     return fail(h, GR00T_E_UNCAPTURED, "shape (B=" + std::to_string(in->batch) + ", L=" + std::to_string(in->vl_len) +
                                            ") was not prepared");
@@ -922,7 +1009,7 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
     rc = run_steps(h, in->batch, in->vl_len, 0, h->cfg.num_steps, true, s);
     if (rc != GR00T_OK) return rc;
   }
-  HIPCHK(h, launch_output(h->w.x, in->action_mask, h->w.bad, action_pred, in->batch,
+  LAUNCH(h, s, K_SMALL, launch_output(h->w.x, in->action_mask, h->w.bad, action_pred, in->batch,
                           h->cfg.action_horizon * h->cfg.action_dim, s));
   HIPCHK(h, hipMemcpyAsync(h->bad_host, h->w.bad, in->batch, hipMemcpyDeviceToHost, s));
   HIPCHK(h, hipEventRecord(h->bad_event, s));
@@ -959,11 +1046,43 @@ void gr00t_destroy(gr00t_head* h) {
     (void)hipStreamDestroy(h->cap_stream);
   }
   if (h->bad_event) (void)hipEventDestroy(h->bad_event);
+  for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   if (h->bad_host) (void)hipHostFree(h->bad_host);
   if (h->arena || h->wsbase) (void)hipDeviceSynchronize();
   if (h->arena) (void)hipFree(h->arena);
   if (h->wsbase) (void)hipFree(h->wsbase);
   delete h;
+}
+
+int gr00t_profile_enable(gr00t_head* h, int on) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (h->prof_on) {
+    int rc = prof_collect(h);
+    if (rc != GR00T_OK) return rc;
+  }
+  h->prof_on = on != 0;
+  h->prof_n.assign(K_NCLASS, 0);
+  h->prof_ms.assign(K_NCLASS, 0.0);
+  return GR00T_OK;
+}
+
+int gr00t_profile_read(gr00t_head* h, int kclass, int64_t* launches, double* total_ms) {
+  if (!h || !launches || !total_ms) return GR00T_E_INVALID_ARG;
+  if (kclass < 0 || kclass >= K_NCLASS) return fail(h, GR00T_E_INVALID_ARG, "kclass out of range");
+  if (h->prof_n.empty()) {
+    h->prof_n.assign(K_NCLASS, 0);
+    h->prof_ms.assign(K_NCLASS, 0.0);
+  }
+  int rc = prof_collect(h);
+  if (rc != GR00T_OK) return rc;
+  *launches = h->prof_n[kclass];
+  *total_ms = h->prof_ms[kclass];
+  return GR00T_OK;
+}
+
+const char* gr00t_profile_class_name(int kclass) {
+  if (kclass < 0 || kclass >= K_NCLASS) return nullptr;
+  return kClassNames[kclass];
 }
 
 const char* gr00t_last_error(const gr00t_head* h) {

@@ -27,7 +27,8 @@ STATUS = {
 
 # Every exported symbol of include/gr00t_head.h.
 EXPORTS = ("gr00t_create", "gr00t_load_weights", "gr00t_finalize", "gr00t_prepare", "gr00t_get_action",
-           "gr00t_velocity", "gr00t_destroy", "gr00t_last_error", "gr00t_device_bytes")
+           "gr00t_velocity", "gr00t_destroy", "gr00t_last_error", "gr00t_device_bytes",
+           "gr00t_profile_enable", "gr00t_profile_read", "gr00t_profile_class_name")
 
 
 class Gr00tConfig(ctypes.Structure):
@@ -81,6 +82,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gr00t_last_error.restype = c_char_p
     lib.gr00t_device_bytes.argtypes = [c_void_p]
     lib.gr00t_device_bytes.restype = c_size_t
+    lib.gr00t_profile_enable.argtypes = [c_void_p, c_int]
+    lib.gr00t_profile_enable.restype = c_int
+    lib.gr00t_profile_read.argtypes = [c_void_p, c_int, POINTER(c_int64), POINTER(ctypes.c_double)]
+    lib.gr00t_profile_read.restype = c_int
+    lib.gr00t_profile_class_name.argtypes = [c_int]
+    lib.gr00t_profile_class_name.restype = c_char_p
     _lib = lib
     return lib
 
@@ -182,6 +189,23 @@ class Gr00tHead:
         inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, None, None)
         self._check(self.lib.gr00t_velocity(self.h, ctypes.byref(inp), step_k, c_void_p(out.data_ptr()),
                                             self._stream(stream)))
+        return out
+
+    def profile(self, on: bool = True):
+        self._check(self.lib.gr00t_profile_enable(self.h, 1 if on else 0))
+
+    def profile_read(self) -> dict:
+        """{class name: (launches, total ms)} of the launches recorded since profile(True)."""
+        out = {}
+        k = 0
+        while True:
+            name = self.lib.gr00t_profile_class_name(k)
+            if name is None:
+                break
+            n, ms = c_int64(), ctypes.c_double()
+            self._check(self.lib.gr00t_profile_read(self.h, k, ctypes.byref(n), ctypes.byref(ms)))
+            out[name.decode()] = (int(n.value), float(ms.value))
+            k += 1
         return out
 
     def device_bytes(self) -> int:

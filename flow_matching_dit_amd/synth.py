@@ -20,6 +20,7 @@ and bias is N(0, 0.02^2); the vision-language LayerNorm gain is 1 + N(0, 0.02^2)
 from __future__ import annotations
 
 from collections import OrderedDict
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import asdict, dataclass, replace
 from typing import Dict, Optional
 
@@ -165,16 +166,24 @@ def weight_shapes(cfg: HeadConfig) -> "OrderedDict[str, tuple]":
     return s
 
 
-def make_weights(w: Workload, seed: int = WEIGHT_SEED) -> "OrderedDict[str, np.ndarray]":
-    """fp32 master weights, N(0, 0.02^2) each; LayerNorm gain 1 + N(0, 0.02^2)."""
-    out = OrderedDict()
-    for idx, (name, shape) in enumerate(weight_shapes(w.cfg).items()):
+def make_weights(w: Workload, seed: int = WEIGHT_SEED, threads: int = 8) -> "OrderedDict[str, np.ndarray]":
+    """fp32 master weights, N(0, 0.02^2) each; LayerNorm gain 1 + N(0, 0.02^2).
+
+    Each tensor has its own stream, so drawing them on several threads gives the
+    same arrays as drawing them in order."""
+    items = list(weight_shapes(w.cfg).items())
+
+    def draw(idx):
+        name, shape = items[idx]
         a = _rng(seed, w.wid, idx).standard_normal(shape, dtype=np.float32)
         a *= np.float32(0.02)
         if name == "vlln.gamma":
             a += np.float32(1.0)
-        out[name] = a
-    return out
+        return a
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        arrays = list(ex.map(draw, range(len(items))))
+    return OrderedDict((name, a) for (name, _), a in zip(items, arrays))
 
 
 def make_inputs(w: Workload, seed: int = INPUT_SEED) -> Dict[str, Optional[np.ndarray]]:

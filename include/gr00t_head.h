@@ -175,6 +175,22 @@ const char* gr00t_last_error(const gr00t_head* h);
 /* Bytes of device memory held by the handle after finalize (weights + workspace). */
 size_t gr00t_device_bytes(const gr00t_head* h);
 
+/*
+ * Launch timing (tracing support). With profiling on, get_action and velocity run
+ * without the graph and bracket every kernel launch with a pair of HIP events on
+ * the call's stream, accumulated per kernel class (vision-language LayerNorm, K/V
+ * projection, adaLN, q/qkv projection, self/cross attention, o projection, norm3,
+ * MLP up/down, output projection, per-embodiment linears, small kernels).
+ *   gr00t_profile_enable: on != 0 starts recording (and clears the totals).
+ *   gr00t_profile_read: synchronises the recorded events, then returns the number of
+ *     launches and their summed duration in ms for class `kclass`; E_INVALID_ARG past
+ *     the last class.
+ *   gr00t_profile_class_name: static name of class `kclass`, NULL past the last one.
+ */
+int gr00t_profile_enable(gr00t_head* h, int on);
+int gr00t_profile_read(gr00t_head* h, int kclass, int64_t* launches, double* total_ms);
+const char* gr00t_profile_class_name(int kclass);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,7 @@ the end-to-end value is "parity unpinned".
 from __future__ import annotations
 
 import math
+from concurrent.futures import ThreadPoolExecutor
 from typing import Callable, Dict, Optional
 
 import numpy as np
@@ -320,18 +321,21 @@ def is_fp8_matrix(name: str) -> bool:
     return name.startswith("blocks.") and name.endswith(FP8_MATRIX_SUFFIXES)
 
 
-def effective_params(cfg, weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
-    """Parameters as float64 values of what the GPU path stores."""
+def effective_params(cfg, weights: Dict[str, np.ndarray], threads: int = 8) -> Dict[str, np.ndarray]:
+    """Parameters as float64 values of what the GPU path stores (tensors are converted
+    independently, on several threads)."""
     prec = cfg["precision"]
-    P = {}
-    for name, w in weights.items():
+
+    def convert(item):
+        name, w = item
         if prec == "fp32":
-            P[name] = np.asarray(w, dtype=np.float64)
-        elif prec == "fp8" and is_fp8_matrix(name):
-            P[name] = quantize_e4m3_columns(w)[0]
-        else:
-            P[name] = round_bf16(w)
-    return P
+            return name, np.asarray(w, dtype=np.float64)
+        if prec == "fp8" and is_fp8_matrix(name):
+            return name, quantize_e4m3_columns(w)[0]
+        return name, round_bf16(w)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        return dict(ex.map(convert, list(weights.items())))
 
 
 def effective_vl(cfg, vl_features):

@@ -2,16 +2,22 @@
 //
 //  * gemm_mfma_kernel: bf16 activations x (bf16 | e4m3) weights on the matrix cores
 //    (v_mfma_f32_16x16x32_bf16), fp32 accumulation. Tiles of A [BM x 64] and
-//    W [BN x 64] are staged through LDS, double buffered, with the next tile's
-//    global loads issued before the current tile's MFMAs. e4m3 weights are decoded
-//    to bf16 (exactly) on their way into LDS; the per-column scale is applied in the
-//    epilogue. Serves the DiT projections, the VL key/value projection and the
-//    per-embodiment linears of width D.
+//    W [BN x 64] go global -> registers -> LDS (double buffered; the next tile's
+//    buffer loads are in flight while the current tile's MFMAs run). Loads use
+//    buffer descriptors, so rows or k beyond the matrix read as zero without
+//    branches. e4m3 weights are decoded to bf16 (exactly) on their way into LDS and
+//    the per-column scale is applied in the epilogue.
+//    The MFMA computes C^T = W A^T per 16x16 fragment, so every lane ends with four
+//    consecutive output columns of one row: the epilogue stores 8 or 16 bytes per lane.
+//    Workgroups are numbered so that consecutive tiles share weight columns and land
+//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs).
+//    Optional split-K writes fp32 partial sums that the next LayerNorm reduces in a
+//    fixed order (deterministic).
 //  * gemm_valu_kernel: fp32 FMA on the vector ALUs for any (A, W) storage types.
 //    Serves the fp32 path, the input-independent tables and the per-embodiment
 //    linears whose K or N is the small action/state width.
 //
-// Both read a group/category description (GemmArgs) so one launch covers the
+// Both read a group/category description (GemmArgs), so one launch covers the
 // per-sample weight gather of the per-embodiment linear (the batched product over
 // W[ids] on the architecture page, "Embodiment-specific projectors"), and finish
 // with a fused epilogue (bias, activation, residual add, head-major scatter, Euler).
@@ -19,6 +25,8 @@
 #include "kernels.h"
 
 namespace gr00t {
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float apply_act(int act, float v) {
   switch (act) {
@@ -29,45 +37,102 @@ __device__ __forceinline__ float apply_act(int act, float v) {
   }
 }
 
-__device__ __forceinline__ void epi_apply(const Epi& e, int g, int r, int n, float v, int cat) {
-  if (e.add_tab) v += e.add_tab[(long)cat * e.add_cstride + n];
-  v = apply_act(e.act, v);
+// Epilogue of NV consecutive columns n .. n+NV-1 of row r in group g (values already
+// scaled and biased). NV is 1 (VALU kernel) or 4 (MFMA kernel).
+template <int EK, int NV>
+__device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, float (&v)[NV], int cat, int split) {
+  if (e.add_tab) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) v[q] += e.add_tab[(long)cat * e.add_cstride + n + q];
+  }
+  if (EK != EPI_PARTIAL) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) v[q] = apply_act(e.act, v[q]);
+  }
   const long row = (long)g * e.out_gstride + e.out_row_off + r;
-  switch (e.kind) {
-    case EPI_STORE: {
-      const long idx = row * e.out_ld + n;
-      if (e.out_f32) ((float*)e.out)[idx] = v;
-      else st((bf16*)e.out + idx, v);
-    } break;
-    case EPI_RESID_ADD: {
-      float* p = (float*)e.out + row * e.out_ld + n;
-      *p = *p + v;
-    } break;
-    case EPI_EULER: {
-      float* p = (float*)e.out + row * e.out_ld + n;
-      *p = *p + e.dt * v;
-    } break;
-    case EPI_HEADS: {
-      const int sec = n / e.width;
-      const int which = sec % e.nwhich;
-      const int layer = sec / e.nwhich;
-      const int c = n - sec * e.width;
-      const int head = c / e.hd;
-      const int d = c - head * e.hd;
-      const int b = (int)(row / e.pos_per_b);
-      const int pos = (int)(row - (long)b * e.pos_per_b);
-      const long idx = (long)layer * e.layer_stride +
-                       (((long)b * e.nh + head) * e.pos_per_b + pos) * e.hd + d;
-      if (e.out_f32) ((float*)e.heads[which])[idx] = v;
-      else st((bf16*)e.heads[which] + idx, v);
-    } break;
+  if (EK == EPI_STORE) {
+    const long idx = row * e.out_ld + n;
+    if (e.out_f32) {
+      float* p = (float*)e.out + idx;
+      if (NV == 4) *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+      else
+#pragma unroll
+        for (int q = 0; q < NV; ++q) p[q] = v[q];
+    } else {
+      uint16_t* p = (uint16_t*)e.out + idx;
+      if (NV == 4) {
+        *(uint2*)p = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
+                                (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+      } else {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) p[q] = f_to_bf16(v[q]);
+      }
+    }
+  } else if (EK == EPI_RESID_ADD || EK == EPI_EULER) {
+    float* p = (float*)e.out + row * e.out_ld + n;
+    const float s = (EK == EPI_EULER) ? e.dt : 1.0f;
+    if (NV == 4) {
+      float4 o = *(float4*)p;
+      o.x += s * v[0];
+      o.y += s * v[1];
+      o.z += s * v[2];
+      o.w += s * v[3];
+      *(float4*)p = o;
+    } else {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) p[q] = p[q] + s * v[q];
+    }
+  } else if (EK == EPI_PARTIAL) {
+    float* p = (float*)e.out + (long)split * e.split_stride + row * e.out_ld + n;
+    if (NV == 4) *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    else
+#pragma unroll
+      for (int q = 0; q < NV; ++q) p[q] = v[q];
+  } else {  // EPI_HEADS: NV consecutive columns stay inside one head (hd % 4 == 0)
+    const int sec = n / e.width;
+    const int which = sec % e.nwhich;
+    const int layer = sec / e.nwhich;
+    const int c = n - sec * e.width;
+    const int head = c / e.hd;
+    const int d = c - head * e.hd;
+    const int b = (int)(row / e.pos_per_b);
+    const int pos = (int)(row - (long)b * e.pos_per_b);
+    const long bh = (long)b * e.nh + head;
+    const long ps = e.pstride[which];
+    const long base = (long)layer * e.layer_stride[which];
+    if (e.transposed[which]) {
+      const long idx = base + (bh * e.hd + d) * ps + pos;
+      if (e.out_f32) {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) ((float*)e.heads[which])[idx + q * ps] = v[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) ((uint16_t*)e.heads[which])[idx + q * ps] = f_to_bf16(v[q]);
+      }
+    } else {
+      const long idx = base + (bh * ps + pos) * e.hd + d;
+      if (e.out_f32) {
+        float* p = (float*)e.heads[which] + idx;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) p[q] = v[q];
+      } else {
+        uint16_t* p = (uint16_t*)e.heads[which] + idx;
+        if (NV == 4) {
+          *(uint2*)p = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
+                                  (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+        } else {
+#pragma unroll
+          for (int q = 0; q < NV; ++q) p[q] = f_to_bf16(v[q]);
+        }
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------
 // Vector-ALU GEMM: 64 x 64 tile, 256 threads, 4 x 4 outputs per thread.
 // ------------------------------------------------------------------------------------
-template <typename TA, typename TW>
+template <typename TA, typename TW, int EK>
 __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float As[BK][BM + 4];
@@ -111,95 +176,145 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + ty * 4 + i;
-    if (r >= a.rows) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
-      if (n >= a.N) continue;
-      float v = acc[i][j];
-      if (a.wscale) v *= a.wscale[(long)cat * a.s_cstride + n];
-      if (a.bias) v += a.bias[(long)cat * a.b_cstride + n];
-      epi_apply(e, g, r, n, v, cat);
+      if (r < a.rows && n < a.N) {
+        float v[1] = {acc[i][j]};
+        if (a.wscale) v[0] *= a.wscale[(long)cat * a.s_cstride + n];
+        if (a.bias) v[0] += a.bias[(long)cat * a.b_cstride + n];
+        epi_store<EK, 1>(e, g, r, n, v, cat, 0);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// MFMA GEMM. Block tile BM x BN, BK = 64, waves arranged WM x WN, each wave owning a
-// (BM/WM) x (BN/WN) sub-tile made of 16 x 16 MFMA fragments.
-//
-// v_mfma_f32_16x16x32_bf16 operand layout (wave64): A fragment (16 rows x 32 k): lane l
-// holds row l%16, k = 8*(l/16) .. +7; B fragment (32 k x 16 cols): lane l holds column
-// l%16, the same k range; the 16 x 16 fp32 result: lane l holds column l%16, rows
-// 4*(l/16) .. +3.
+// MFMA GEMM
 // ------------------------------------------------------------------------------------
 constexpr int MF_BK = 64;
 constexpr int MF_LDS_LD = MF_BK + 8;  // bf16 elements per LDS row (16 B pad: conflict-free b128 reads)
+constexpr int OOB = 0x7FFFFFF0;       // buffer offset that is always out of range (reads 0)
 
-template <int BM, int BN, int WM, int WN, bool FP8>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  int32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// e4m3 code -> bf16 bits without branches.
+__device__ __forceinline__ uint32_t e4m3_bf16_nb(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 0x7u;
+  const uint32_t normal = s | ((e + 120u) << 7) | (m << 4);
+  const uint32_t sub = s | (__float_as_uint((float)m * (1.0f / 512.0f)) >> 16);
+  return e ? normal : sub;
+}
+
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return e4m3_bf16_nb(w & 0xFF) | (e4m3_bf16_nb((w >> 8) & 0xFF) << 16);
+}
+
+// Map the linear workgroup id to (tile_m, tile_n): ids are first regrouped so that each
+// XCD (id % 8) receives a contiguous range, then ranges walk GM m-tiles fastest so that
+// neighbouring workgroups reuse the same weight columns from the XCD's L2.
+__device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
+  const int nb = nm * nn;
+  const int id = blockIdx.x;
+  // bijective regrouping: XCD x (= id % 8) owns the contiguous range starting at
+  // x * q + min(x, r), where q = nb / 8 and r = nb % 8
+  const int q = nb >> 3, r = nb & 7;
+  const int x = id & 7;
+  const int lid = x * q + min(x, r) + (id >> 3);
+  const int GM = 16;
+  const int group = lid / (GM * nn);
+  const int first = group * GM;
+  const int gm = min(GM, nm - first);
+  const int in = lid - group * GM * nn;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <int BM, int BN, int WM, int WN, bool FP8, int EK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi e) {
   constexpr int NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 fragment");
-  constexpr int A_CHUNKS = BM * 8;                      // 16-byte chunks of bf16
-  constexpr int B_CHUNKS = FP8 ? BN * 4 : BN * 8;       // 16-byte chunks of W
+  constexpr int A_CHUNKS = BM * 8;                 // 16-byte chunks of bf16
+  constexpr int B_CHUNKS = FP8 ? BN * 4 : BN * 8;  // 16-byte chunks of W
   constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
   constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * MF_LDS_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * MF_LDS_LD];
 
-  const int g = blockIdx.z;
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(nm, nn, tm, tn);
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
-  const int r0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int r0 = tm * BM, n0 = tn * BN;
+  const int kper = a.k_per_split;
+  const int kbeg = split * kper;
+  const int kend = min(a.K, kbeg + kper);
+
   const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
-  const uint8_t* W8 = (const uint8_t*)a.W + (long)cat * a.w_cstride;          // FP8
-  const uint16_t* W16 = (const uint16_t*)a.W + (long)cat * a.w_cstride;       // bf16
+  const uint32_t wes = FP8 ? 1 : 2;
+  const char* Wb = (const char*)a.W + (long)cat * a.w_cstride * wes;
+  // Descriptors cover exactly the valid rows of this group: everything past them reads 0.
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(Wb, (uint32_t)((long)a.N * a.K * wes));
+
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int wm = wave / WN, wn = wave % WN;
 
-  uint4 ra[A_PER], rb[B_PER];
+  // Per-thread global byte offsets of its chunks at k = 0 (OOB for chunks past the tile).
+  int aoff[A_PER], boff[B_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int c = t + i * NT;
+    const int row = c >> 3, kc = (c & 7) * 8;
+    aoff[i] = (c < A_CHUNKS && r0 + row < a.rows) ? ((r0 + row) * (int)a.lda + kc) * 2 : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const int c = t + i * NT;
+    if (FP8) {
+      const int n = c >> 2, kc = (c & 3) * 16;
+      boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) : OOB;
+    } else {
+      const int n = c >> 3, kc = (c & 7) * 8;
+      boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) * 2 : OOB;
+    }
+  }
 
+  uint4 ra[A_PER], rb[B_PER];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int c = t + i * NT;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < A_CHUNKS) {
-        const int row = c >> 3, kc = (c & 7) * 8;
-        const int gr = r0 + row;
-        if (gr < a.rows && k0 + kc < a.K) v = *(const uint4*)(A + (long)gr * a.lda + k0 + kc);
-      }
-      ra[i] = v;
+      const int kc = ((t + i * NT) & 7) * 8;
+      const bool in = aoff[i] != OOB && k0 + kc < kend;
+      ra[i] = buf_load16(ra_rsrc, in ? aoff[i] + k0 * 2 : OOB);
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
-      const int c = t + i * NT;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < B_CHUNKS) {
-        if (FP8) {
-          const int n = c >> 2, kc = (c & 3) * 16;
-          const int gn = n0 + n;
-          if (gn < a.N && k0 + kc < a.K) v = *(const uint4*)(W8 + (long)gn * a.K + k0 + kc);
-        } else {
-          const int n = c >> 3, kc = (c & 7) * 8;
-          const int gn = n0 + n;
-          if (gn < a.N && k0 + kc < a.K) v = *(const uint4*)(W16 + (long)gn * a.K + k0 + kc);
-        }
-      }
-      rb[i] = v;
+      const int kc = FP8 ? ((t + i * NT) & 3) * 16 : ((t + i * NT) & 7) * 8;
+      const bool in = boff[i] != OOB && k0 + kc < kend;
+      rb[i] = buf_load16(rw_rsrc, in ? boff[i] + k0 * (int)wes : OOB);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       const int c = t + i * NT;
-      if (c < A_CHUNKS) {
-        const int row = c >> 3, kc = (c & 7) * 8;
-        *(uint4*)&As[buf][row * MF_LDS_LD + kc] = ra[i];
-      }
+      if (c < A_CHUNKS) *(uint4*)&As[buf][(c >> 3) * MF_LDS_LD + (c & 7) * 8] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
@@ -207,19 +322,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
       if (c < B_CHUNKS) {
         if (FP8) {
           const int n = c >> 2, kc = (c & 3) * 16;
-          const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-          uint32_t o[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            o[2 * q] = (uint32_t)e4m3_to_bf16(w[q] & 0xFF) | ((uint32_t)e4m3_to_bf16((w[q] >> 8) & 0xFF) << 16);
-            o[2 * q + 1] =
-                (uint32_t)e4m3_to_bf16((w[q] >> 16) & 0xFF) | ((uint32_t)e4m3_to_bf16(w[q] >> 24) << 16);
-          }
-          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc] = make_uint4(o[0], o[1], o[2], o[3]);
-          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc + 8] = make_uint4(o[4], o[5], o[6], o[7]);
+          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc] = make_uint4(e4m3x2_to_bf16x2(rb[i].x), e4m3x2_to_bf16x2(rb[i].x >> 16),
+                                                             e4m3x2_to_bf16x2(rb[i].y), e4m3x2_to_bf16x2(rb[i].y >> 16));
+          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc + 8] = make_uint4(e4m3x2_to_bf16x2(rb[i].z), e4m3x2_to_bf16x2(rb[i].z >> 16),
+                                                                 e4m3x2_to_bf16x2(rb[i].w), e4m3x2_to_bf16x2(rb[i].w >> 16));
         } else {
-          const int n = c >> 3, kc = (c & 7) * 8;
-          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc] = rb[i];
+          *(uint4*)&Bs[buf][(c >> 3) * MF_LDS_LD + (c & 7) * 8] = rb[i];
         }
       }
     }
@@ -231,45 +339,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = (a.K + MF_BK - 1) / MF_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  const int nk = (kend - kbeg + MF_BK - 1) / MF_BK;
+  if (nk > 0) {
+    gload(kbeg);
+    lstore(0);
+    __syncthreads();
+  }
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * MF_BK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * MF_BK);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
+      bf16x8_t af[FM], wf[FN];
       const int koff = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         af[i] = *(const bf16x8_t*)&As[buf][(wm * TM + i * 16 + (lane & 15)) * MF_LDS_LD + koff];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN + j * 16 + (lane & 15)) * MF_LDS_LD + koff];
+        wf[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN + j * 16 + (lane & 15)) * MF_LDS_LD + koff];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
   }
 
+  // acc[i][j][q]: row m = r0 + wm*TM + i*16 + lane%16, column n = n0 + wn*TN + j*16 + 4*(lane/16) + q
+  const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * TN + j * 16 + (lane & 15);
+    const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
     if (n >= a.N) continue;
-    const float sc = a.wscale ? a.wscale[(long)cat * a.s_cstride + n] : 1.0f;
-    const float bi = a.bias ? a.bias[(long)cat * a.b_cstride + n] : 0.0f;
+    float sc[4], bi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+      bi[q] = (a.bias && add_bias) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const int r = r0 + wm * TM + i * 16 + (lane & 15);
+      if (r < a.rows) {
+        float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = r0 + wm * TM + i * 16 + (lane >> 4) * 4 + q;
-        if (r < a.rows) epi_apply(e, g, r, n, acc[i][j][q] * sc + bi, cat);
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
+        epi_store<EK, 4>(e, g, r, n, v, cat, split);
       }
     }
   }
@@ -281,7 +399,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 template <typename TA, typename TW>
 static hipError_t valu_go(const GemmArgs& a, const Epi& e, hipStream_t s) {
   dim3 grid((a.N + 63) / 64, (a.rows + 63) / 64, a.groups);
-  hipLaunchKernelGGL((gemm_valu_kernel<TA, TW>), grid, dim3(256), 0, s, a, e);
+  switch (e.kind) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_valu_kernel<TA, TW, EPI_STORE>), grid, dim3(256), 0, s, a, e); break;
+    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_valu_kernel<TA, TW, EPI_RESID_ADD>), grid, dim3(256), 0, s, a, e); break;
+    case EPI_HEADS: hipLaunchKernelGGL((gemm_valu_kernel<TA, TW, EPI_HEADS>), grid, dim3(256), 0, s, a, e); break;
+    case EPI_EULER: hipLaunchKernelGGL((gemm_valu_kernel<TA, TW, EPI_EULER>), grid, dim3(256), 0, s, a, e); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -291,32 +415,76 @@ hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt,
   if (at == DT_F32 && wt == DT_BF16) return valu_go<float, bf16>(a, e, s);
   if (at == DT_BF16 && wt == DT_BF16) return valu_go<bf16, bf16>(a, e, s);
   if (at == DT_BF16 && wt == DT_F32) return valu_go<bf16, float>(a, e, s);
-  if (at == DT_F32 && wt == DT_FP8) return valu_go<float, fp8e4m3>(a, e, s);
-  if (at == DT_BF16 && wt == DT_FP8) return valu_go<bf16, fp8e4m3>(a, e, s);
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, hipStream_t s) {
-  dim3 grid((a.N + BN - 1) / BN, (a.rows + BM - 1) / BM, a.groups);
-  if (fp8)
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, true>), grid, dim3(64 * WM * WN), 0, s, a, e);
-  else
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, false>), grid, dim3(64 * WM * WN), 0, s, a, e);
+template <int BM, int BN, int WM, int WN, bool FP8>
+static hipError_t mfma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  dim3 grid(nm * nn, a.groups, splits);
+  dim3 blk(64 * WM * WN);
+  switch (e.kind) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_STORE>), grid, blk, 0, s, a, e); break;
+    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_RESID_ADD>), grid, blk, 0, s, a, e); break;
+    case EPI_HEADS: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_HEADS>), grid, blk, 0, s, a, e); break;
+    case EPI_EULER: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_EULER>), grid, blk, 0, s, a, e); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_PARTIAL>), grid, blk, 0, s, a, e); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a, const Epi& e, DType wt, hipStream_t s) {
+template <int BM, int BN, int WM, int WN>
+static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
+  return fp8 ? mfma_kind<BM, BN, WM, WN, true>(a, e, splits, s) : mfma_kind<BM, BN, WM, WN, false>(a, e, splits, s);
+}
+
+// 0: 256x128 (8 waves), 1: 128x128, 2: 64x128, 3: 32x64, 4: 16x64
+static int tile_choice(int rows, int N, int groups) {
+  auto tiles = [&](int bm, int bn) { return (long)((rows + bm - 1) / bm) * ((N + bn - 1) / bn) * groups; };
+  if (rows <= 16) return 4;
+  if (rows <= 32) return 3;
+  if (rows <= 64) return 2;
+  if (tiles(256, 128) >= 512) return 0;
+  if (tiles(128, 128) >= 256) return 1;
+  return 2;
+}
+
+// Smallest split count that gives >= 240 workgroups (or leaves <= 512 k per split),
+// else the largest valid one (at most 8, each split a multiple of 64 deep).
+int gemm_mfma_splits(int rows, int N, int K, int groups) {
+  static const int bm[5] = {256, 128, 64, 32, 16}, bn[5] = {128, 128, 128, 64, 64};
+  int best = 1;
+  for (int s = 1; s <= 8; ++s) {
+    if (K % (64 * s) != 0) continue;
+    best = s;
+    const int c = tile_choice(rows, N, groups * s);
+    const long t = (long)((rows + bm[c] - 1) / bm[c]) * ((N + bn[c] - 1) / bn[c]) * groups * s;
+    if (t >= 240 || K / s <= 512) return s;
+  }
+  return best;
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStream_t s) {
+  GemmArgs a = a_in;
   if (a.rows <= 0 || a.N <= 0 || a.groups <= 0) return hipSuccess;
-  if ((a.K % 8) != 0 || (a.lda % 8) != 0) return hipErrorInvalidValue;
   const bool fp8 = (wt == DT_FP8);
   if (!fp8 && wt != DT_BF16) return hipErrorInvalidValue;
-  if (fp8 && (a.K % 16) != 0) return hipErrorInvalidValue;
-  const long tiles128 = (long)((a.N + 127) / 128) * ((a.rows + 127) / 128) * a.groups;
-  if (a.rows <= 16) return mfma_go<16, 64, 1, 4>(a, e, fp8, s);
-  if (a.rows <= 32) return mfma_go<32, 64, 1, 4>(a, e, fp8, s);
-  if (a.rows <= 64 || tiles128 < 256) return mfma_go<64, 128, 2, 2>(a, e, fp8, s);
-  return mfma_go<128, 128, 2, 2>(a, e, fp8, s);
+  if ((a.K % (fp8 ? 16 : 8)) != 0 || (a.lda % 8) != 0 || (a.N % 4) != 0) return hipErrorInvalidValue;
+  int splits = 1;
+  if (e.kind == EPI_PARTIAL) {
+    splits = e.splits;
+    if (splits < 1 || a.K % (64 * splits) != 0) return hipErrorInvalidValue;
+  }
+  a.k_per_split = a.K / splits;
+  if ((long)a.rows * a.lda * 2 >= (1l << 31) || (long)a.N * a.K * 2 >= (1l << 31)) return hipErrorInvalidValue;
+  switch (tile_choice(a.rows, a.N, a.groups * splits)) {
+    case 0: return mfma_go<256, 128, 4, 2>(a, e, fp8, splits, s);
+    case 1: return mfma_go<128, 128, 2, 2>(a, e, fp8, splits, s);
+    case 2: return mfma_go<64, 128, 2, 2>(a, e, fp8, splits, s);
+    case 3: return mfma_go<32, 64, 1, 4>(a, e, fp8, splits, s);
+    default: return mfma_go<16, 64, 1, 4>(a, e, fp8, splits, s);
+  }
 }
 
 }  // namespace gr00t

@@ -115,7 +115,7 @@ struct Layout {
 struct Ws {  // workspace pointers
   float* h;
   void *n, *q, *k, *v, *o, *u, *y, *e1, *e2, *se1, *vln, *kc, *vc;
-  float *x, *s, *vout;
+  float *x, *s, *vout, *part;
   uint8_t *code, *bad;
   int *ids, *iota;
   float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
@@ -160,6 +160,8 @@ int fail(gr00t_head* h, int code, const std::string& msg) {
 }
 
 size_t act_bytes(const gr00t_head* h) { return h->act == DT_F32 ? 4 : 2; }
+
+int round32(int x) { return (x + 31) / 32 * 32; }
 
 
 std::string shape_str(const std::vector<int64_t>& s) {
@@ -490,9 +492,29 @@ Epi ep_store(void* out, bool f32, long ld, int act = ACT_NONE) {
 }
 
 hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s) {
-  if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0)
+  if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 && a.N % 4 == 0)
     return launch_gemm_mfma(a, e, wt, s);
   return launch_gemm_valu(a, e, at, wt, s);
+}
+
+// h += A W^T + b for the residual stream h: direct residual add, or split-K into the
+// partial buffer (then *pend = number of partials the next norm must add).
+hipError_t resid_gemm(gr00t_head* h, const GemmArgs& a, DType at, DType wt, long pstride, int& pend, hipStream_t s) {
+  Epi e = ep_store(h->w.h, true, a.N);
+  const bool mfma = at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 &&
+                    a.N % 4 == 0;
+  const int splits = mfma ? gemm_mfma_splits(a.rows, a.N, a.K, a.groups) : 1;
+  if (splits > 1) {
+    e.kind = EPI_PARTIAL;
+    e.out = h->w.part;
+    e.splits = splits;
+    e.split_stride = pstride;
+    pend = splits;
+    return launch_gemm_mfma(a, e, wt, s);
+  }
+  e.kind = EPI_RESID_ADD;
+  pend = 0;
+  return gemm(h, a, e, at, wt, s);
 }
 
 // ------------------------------------------------------------------ tables (finalize)
@@ -579,7 +601,11 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     e.nh = c.num_heads;
     e.hd = c.head_dim;
     e.pos_per_b = L;
-    e.layer_stride = (long)B * L * D;
+    const int Lp = round32(L);
+    e.pstride[0] = e.pstride[1] = Lp;
+    e.transposed[0] = 0;
+    e.transposed[1] = 1;  // values cached [hd][L] for the attention's V^T operand
+    e.layer_stride[0] = e.layer_stride[1] = (long)B * Lp * D;
     LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));
   }
   {  // state encoder: one token per sample
@@ -624,6 +650,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
   const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
   const DType dw = c.weight_dtype == GR00T_FP8_E4M3 ? DT_FP8 : mw;  // DiT matrices
   const long M = (long)B * S;
+  const int Sp = round32(S);
   const size_t ab = act_bytes(h);
   (void)C;
   for (int k = k0; k < k1; ++k) {
@@ -665,12 +692,16 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       LAUNCH(h, s, K_ACTION_ENC, gemm(h, a, e, A, mw, s));
       LAUNCH(h, s, K_SMALL, launch_copy_rows(h->w.s, D, h->w.h, D, S, 0, B, D, s));
     }
-    // ---- DiT blocks
+    // ---- DiT blocks. The two residual GEMMs (o projection, MLP down) may run split-K
+    // into fp32 partials; the following norm adds them to h in a fixed order.
+    int pend = 0;  // partial sums not yet added to h
+    const long pstride = M * D;
     for (int l = 0; l < Nl; ++l) {
       const LayerOff& lo = lay.L[l];
       const bool self = (l % 2) == 1;
       const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + l) * 2 * D;
-      LAUNCH(h, s, K_ADALN, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada, s));
+      pend = 0;
       {
         GemmArgs a = ga(h->w.n, D, (int)M, (self ? 3 : 1) * D, D);
         a.W = at<void>(h, lo.wq);
@@ -687,7 +718,9 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         e.nh = nh;
         e.hd = hd;
         e.pos_per_b = S;
-        e.layer_stride = 0;
+        e.pstride[0] = S;
+        e.pstride[1] = e.pstride[2] = Sp;
+        e.transposed[2] = 1;
         LAUNCH(h, s, self ? K_QKV_PROJ : K_Q_PROJ, gemm(h, a, e, A, dw, s));
       }
       AttnArgs at_{};
@@ -699,14 +732,17 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       at_.hd = hd;
       if (self) {
         at_.k = h->w.k;
-        at_.v = h->w.v;
+        at_.vt = h->w.v;
         at_.Lk = S;
+        at_.Lp = Sp;
         at_.mask = nullptr;
       } else {
         const size_t ci = (size_t)(l / 2);
-        at_.k = (const char*)h->w.kc + ci * (size_t)B * L * D * ab;
-        at_.v = (const char*)h->w.vc + ci * (size_t)B * L * D * ab;
+        const int Lp = round32(L);
+        at_.k = (const char*)h->w.kc + ci * (size_t)B * Lp * D * ab;
+        at_.vt = (const char*)h->w.vc + ci * (size_t)B * Lp * D * ab;
         at_.Lk = L;
+        at_.Lp = Lp;
         at_.mask = h->w.code;
         at_.mask_bit = (l % (2 * c.attend_text_every_n_blocks) == 0) ? 1 : 2;
       }
@@ -716,11 +752,10 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         a.W = at<void>(h, lo.wo);
         a.bias = at<float>(h, lo.bo);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.so) : nullptr;
-        Epi e = ep_store(h->w.h, true, D);
-        e.kind = EPI_RESID_ADD;
-        LAUNCH(h, s, K_O_PROJ, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, K_O_PROJ, resid_gemm(h, a, A, dw, pstride, pend, s));
       }
-      LAUNCH(h, s, K_NORM3, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, nullptr, s));
+      LAUNCH(h, s, K_NORM3, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, nullptr, s));
+      pend = 0;
       {
         GemmArgs a = ga(h->w.n, D, (int)M, F, D);
         a.W = at<void>(h, lo.w1);
@@ -731,15 +766,13 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         a.W = at<void>(h, lo.w2);
         a.bias = at<float>(h, lo.b2);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.s2) : nullptr;
-        Epi e = ep_store(h->w.h, true, D);
-        e.kind = EPI_RESID_ADD;
-        LAUNCH(h, s, K_FF_DOWN, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, K_FF_DOWN, resid_gemm(h, a, A, dw, pstride, pend, s));
       }
     }
     // ---- output adaLN + projection, then decoder and Euler update
     {
       const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + Nl) * 2 * D;
-      LAUNCH(h, s, K_ADALN, launch_layernorm(h->w.h, DT_F32, D, h->w.n, A, D, (int)M, D, nullptr, nullptr, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada, s));
       GemmArgs a = ga(h->w.n, D, (int)M, D, D);
       a.W = at<void>(h, lay.p_w);
       a.bias = at<float>(h, lay.p_b);
@@ -919,14 +952,16 @@ int gr00t_finalize(gr00t_head* h) {
   const size_t Bm = c.max_batch, Lm = c.max_vl_len, D = c.hidden, F = c.ff_dim, H = c.action_horizon, S = H + 1;
   const size_t A = c.action_dim, E = c.vl_dim, K = c.num_steps, Nl = c.num_layers, Nc = (Nl + 1) / 2;
   const size_t C = c.num_categories, T = c.time_freq_dim;
+  const size_t Sp = round32((int)S), Lmp = round32((int)Lm);
   const size_t ab = act_bytes(h);
   std::vector<std::pair<void**, size_t>> req = {
       {(void**)&h->w.h, Bm * S * D * 4},      {&h->w.n, Bm * S * D * ab},       {&h->w.q, Bm * S * D * ab},
-      {&h->w.k, Bm * S * D * ab},             {&h->w.v, Bm * S * D * ab},       {&h->w.o, Bm * S * D * ab},
+      {&h->w.k, Bm * Sp * D * ab},            {&h->w.v, Bm * Sp * D * ab},      {&h->w.o, Bm * S * D * ab},
       {&h->w.u, Bm * S * F * ab},             {&h->w.y, Bm * S * D * ab},       {&h->w.e1, Bm * H * D * ab},
       {&h->w.e2, Bm * H * D * ab},            {&h->w.se1, Bm * D * ab},         {&h->w.vln, Bm * Lm * E * ab},
-      {&h->w.kc, Nc * Bm * Lm * D * ab},      {&h->w.vc, Nc * Bm * Lm * D * ab}, {(void**)&h->w.x, Bm * H * A * 4},
+      {&h->w.kc, Nc * Bm * Lmp * D * ab},     {&h->w.vc, Nc * Bm * Lmp * D * ab}, {(void**)&h->w.x, Bm * H * A * 4},
       {(void**)&h->w.s, Bm * D * 4},          {(void**)&h->w.vout, Bm * H * A * 4},
+      {(void**)&h->w.part, 8 * Bm * S * D * 4},
       {(void**)&h->w.code, Bm * Lm},          {(void**)&h->w.bad, Bm},           {(void**)&h->w.ids, Bm * 4},
       {(void**)&h->w.iota, C * 4},            {(void**)&h->w.sin_t, K * T * 4},  {(void**)&h->w.t1, K * D * 4},
       {(void**)&h->w.temb, K * D * 4},        {(void**)&h->w.stemb, K * D * 4},
@@ -949,6 +984,11 @@ int gr00t_finalize(gr00t_head* h) {
   for (size_t i = 0; i < C; ++i) iota[i] = (int)i;
   HIPCHK(h, hipMemcpy(h->w.iota, iota.data(), C * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemset(h->w.bad, 0, Bm));
+  // key/value padding rows and columns are read with weight 0: keep them finite
+  HIPCHK(h, hipMemset(h->w.kc, 0, Nc * Bm * Lmp * D * ab));
+  HIPCHK(h, hipMemset(h->w.vc, 0, Nc * Bm * Lmp * D * ab));
+  HIPCHK(h, hipMemset(h->w.k, 0, Bm * Sp * D * ab));
+  HIPCHK(h, hipMemset(h->w.v, 0, Bm * Sp * D * ab));
   HIPCHK(h, hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
   HIPCHK(h, hipHostMalloc((void**)&h->bad_host, Bm, hipHostMallocDefault));
   HIPCHK(h, hipEventCreateWithFlags(&h->bad_event, hipEventDisableTiming));

@@ -12,7 +12,8 @@ enum EpiKind {
   EPI_STORE = 0,      // out[row, n] = act(v)            (fp32 or bf16 out)
   EPI_RESID_ADD = 1,  // out[row, n] += act(v)           (fp32 residual stream)
   EPI_HEADS = 2,      // scatter to head-major [b][head][pos][hd] buffers (act dtype)
-  EPI_EULER = 3       // out[row, n] += dt * act(v)      (fp32 Euler state)
+  EPI_EULER = 3,      // out[row, n] += dt * act(v)      (fp32 Euler state)
+  EPI_PARTIAL = 4     // out[split][row, n] = v          (fp32 split-K partial sums, bias in split 0)
 };
 
 // C[g, r, n] = sum_k A[g, r, k] * W[id_g][n, k]   (then * wscale[id_g][n] + bias[id_g][n])
@@ -34,6 +35,7 @@ struct GemmArgs {
   int N;
   int K;
   int groups;
+  int k_per_split;      // set by the launcher
 };
 
 struct Epi {
@@ -48,20 +50,27 @@ struct Epi {
   long add_cstride;
   // EPI_HEADS: column n -> section sec = n / width, which = sec % nwhich,
   // layer = sec / nwhich, head = (n % width) / hd, d = n % hd; row r -> (b, pos) with
-  // pos_per_b positions per sample; element goes to
-  // heads[which] + layer * layer_stride + ((b * nh + head) * pos_per_b + pos) * hd + d.
+  // pos_per_b positions per sample; element goes to heads[which] + layer * layer_stride[which] +
+  //   ((b * nh + head) * pstride[which] + pos) * hd + d        (row-major positions), or
+  //   ((b * nh + head) * hd + d) * pstride[which] + pos        (transposed[which]: [hd][pos]).
   void* heads[3];
   int nwhich;
   int width;
   int nh;
   int hd;
   int pos_per_b;
-  long layer_stride;
+  int pstride[3];
+  int transposed[3];
+  long layer_stride[3];
   float dt;             // EPI_EULER
+  int splits;           // EPI_PARTIAL: number of K splits (grid z)
+  long split_stride;    // EPI_PARTIAL: elements between consecutive splits' outputs
 };
 
 hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, const Epi& e, DType wt, hipStream_t s);
+// K splits the MFMA GEMM would use for a split-K launch of this shape (1 = none).
+int gemm_mfma_splits(int rows, int N, int K, int groups);
 
 // LayerNorm over rows of width D (eps 1e-5, population variance):
 //   y = (x - mean) / sqrt(var + eps) [* gamma + beta] [* (1 + scale) + shift]
@@ -70,18 +79,26 @@ hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt
                             int D, const float* gamma, const float* beta, const float* ada,
                             hipStream_t s);
 
+// Residual add of split-K partial sums, then adaLN / LayerNorm:
+//   h[r] += sum_s partials[s][r]  (fixed order, written back), y = LN(h[r]) [* (1 + scale) + shift]
+// partials may be NULL (nsplit = 0): then it is launch_layernorm on fp32 h.
+hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y,
+                                  DType yt, int rows, int D, const float* ada, hipStream_t s);
+
 // Multi-head attention per (sample, head): softmax(q k^T / sqrt(hd)) v.
-// q [B][nh][S][hd], k/v [B][nh][Lk][hd] (act dtype); o [B*S][nh*hd] (act dtype).
+// q [B][nh][S][hd]; k [B][nh][Lp][hd] (keys row-major, Lp = Lk rounded up to 32);
+// vt [B][nh][hd][Lp] (values transposed); o [B*S][nh*hd]; all in act dtype. Key rows
+// and value columns in [Lk, Lp) must hold finite values (they get weight 0).
 // mask: NULL = every key admitted; else key j of sample b is admitted iff
 // (mask[b * Lk + j] & mask_bit) != 0. A query with no admitted key outputs 0.
 struct AttnArgs {
   const void* q;
   const void* k;
-  const void* v;
+  const void* vt;
   void* o;
   const uint8_t* mask;
   int mask_bit;
-  int B, S, Lk, nh, hd;
+  int B, S, Lk, Lp, nh, hd;
 };
 hipError_t launch_attention(const AttnArgs& a, DType t, hipStream_t s);
 

@@ -74,11 +74,74 @@ hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt
   return hipGetLastError();
 }
 
+// Residual add of split-K partial sums fused with the next (ada)LayerNorm: one wave per
+// row; the row of h is updated in place (h + p_0 + p_1 + ..., fixed order) and normalised.
+template <typename TY>
+__global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict__ h, const float* __restrict__ part,
+                                                              int nsplit, long split_stride, TY* __restrict__ y,
+                                                              int rows, int D, const float* __restrict__ ada) {
+  constexpr int MAXPER = 32;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float* hr = h + (long)row * D;
+  float v[MAXPER];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int c = lane + i * 64;
+    float x = 0.0f;
+    if (c < D) {
+      x = hr[c];
+      for (int p = 0; p < nsplit; ++p) x += part[(long)p * split_stride + (long)row * D + c];
+      if (nsplit > 0) hr[c] = x;
+    }
+    v[i] = x;
+    s += x;
+  }
+  const float mean = wave_sum(s) / (float)D;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int c = lane + i * 64;
+    const float d = v[i] - mean;
+    s2 += (c < D) ? d * d : 0.0f;
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)D + 1e-5f);
+  TY* yr = y + (long)row * D;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int c = lane + i * 64;
+    if (c < D) {
+      float o = (v[i] - mean) * rstd;
+      if (ada) o = o * (1.0f + ada[c]) + ada[D + c];
+      st(yr + c, o);
+    }
+  }
+}
+
+hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y, DType yt,
+                                  int rows, int D, const float* ada, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (D > 2048) return hipErrorInvalidValue;
+  if (!partials) nsplit = 0;
+  dim3 grid((rows + 3) / 4);
+  if (yt == DT_F32)
+    hipLaunchKernelGGL((resid_layernorm_kernel<float>), grid, dim3(256), 0, s, h, partials, nsplit, split_stride,
+                       (float*)y, rows, D, ada);
+  else if (yt == DT_BF16)
+    hipLaunchKernelGGL((resid_layernorm_kernel<bf16>), grid, dim3(256), 0, s, h, partials, nsplit, split_stride,
+                       (bf16*)y, rows, D, ada);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------
-// Attention on the vector ALUs: one workgroup per (head, sample); keys streamed in
-// chunks of 64 through LDS with an online (running max / running sum) softmax in
-// fp32. Self-attention blocks pass the S state+action tokens as keys; cross-attention
-// blocks pass the cached VL keys/values with the block's key mask
+// Attention on the vector ALUs (fp32 path): one workgroup per (head, sample); keys
+// streamed in chunks of 64 through LDS with an online (running max / running sum)
+// softmax in fp32. Self-attention blocks pass the S state+action tokens as keys;
+// cross-attention blocks pass the cached VL keys/values with the block's key mask
 // ("AlternateVLDiT variant").
 // ------------------------------------------------------------------------------------
 constexpr int AT_KC = 64;
@@ -97,10 +160,10 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
 
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
-  const int S = a.S, hd = a.hd, Lk = a.Lk, nh = a.nh;
+  const int S = a.S, hd = a.hd, Lk = a.Lk, Lp = a.Lp, nh = a.nh;
   const T* q = (const T*)a.q + (long)(b * nh + h) * S * hd;
-  const T* k = (const T*)a.k + (long)(b * nh + h) * Lk * hd;
-  const T* v = (const T*)a.v + (long)(b * nh + h) * Lk * hd;
+  const T* k = (const T*)a.k + (long)(b * nh + h) * Lp * hd;
+  const T* vt = (const T*)a.vt + (long)(b * nh + h) * hd * Lp;
   const float scale = 1.0f / sqrtf((float)hd);
 
   for (int i = t; i < S * hd; i += 256) Qs[i / hd][i % hd] = ld(q + i) * scale;
@@ -119,7 +182,10 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
       const int jj = i / hd, d = i - jj * hd;
       const bool in = jj < nk;
       Ks[jj][d] = in ? ld(k + (long)(j0 + jj) * hd + d) : 0.0f;
-      Vs[jj][d] = in ? ld(v + (long)(j0 + jj) * hd + d) : 0.0f;
+    }
+    for (int i = t; i < AT_KC * hd; i += 256) {
+      const int d = i / AT_KC, jj = i - d * AT_KC;
+      Vs[jj][d] = (jj < nk) ? ld(vt + (long)d * Lp + j0 + jj) : 0.0f;
     }
     if (t < AT_KC) adm[t] = (t < nk) && (a.mask == nullptr || (a.mask[(long)b * Lk + j0 + t] & a.mask_bit));
     __syncthreads();
@@ -174,17 +240,199 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Attention on the matrix cores (bf16): one workgroup (4 waves) per (head, sample);
+// wave w takes the 32-key tiles w, w+4, ... For a tile, S^T = K Q^T is formed per
+// 16-query fragment with v_mfma_f32_16x16x32_bf16, so each lane holds the scores of
+// one query against 8 keys; the tile's keys are enumerated so that those 8 keys are
+// contiguous, which makes the exponentiated scores directly the B operand of
+// O^T += V^T P^T (values cached transposed, [hd][L]). Running max / sum in fp32 with
+// exp2; tiles with no admitted key are skipped; the 4 waves' partial results are
+// merged through LDS at the end.
+// ------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
+  return ok ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
+}
+
+template <int HD, int QF>
+__global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
+  constexpr int KS = (HD + 31) / 32;  // 32-wide k steps over the head dim (zero padded)
+  constexpr int HF = HD / 16;         // 16-row fragments of the head dim
+  __shared__ float red_m[4][QF * 16];
+  __shared__ float red_l[4][QF * 16];
+  __shared__ float red_o[4][QF * 16][HD + 1];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int S = a.S, Lk = a.Lk, Lp = a.Lp, nh = a.nh;
+  const long bh = (long)b * nh + h;
+  const uint16_t* q = (const uint16_t*)a.q + bh * S * HD;
+  const uint16_t* k = (const uint16_t*)a.k + bh * Lp * HD;
+  const uint16_t* vt = (const uint16_t*)a.vt + bh * HD * Lp;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+
+  // Q^T fragments: lane holds query qf*16 + c16, head dims 32*ks + 8g .. +7
+  bf16x8_v qfr[QF][KS];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int qi = qf * 16 + c16, d0 = ks * 32 + g * 8;
+      qfr[qf][ks] = __builtin_bit_cast(bf16x8_v, ld16_or_zero(q + (long)qi * HD + d0, qi < S && d0 < HD));
+    }
+
+  floatx4_t acc[QF][HF];
+  float m[QF], l[QF];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    m[qf] = -INFINITY;
+    l[qf] = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf) acc[qf][hf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int ntiles = (Lk + 31) / 32;
+  for (int kt = wave; kt < ntiles; kt += 4) {
+    const int base = kt * 32;
+    bool admit = false;
+    if (lane < 32) {
+      const int j = base + lane;
+      admit = j < Lk && (a.mask == nullptr || (a.mask[(long)b * Lk + j] & a.mask_bit));
+    }
+    const unsigned long long bal = __ballot(admit);
+    if (bal == 0ull) continue;
+    // K fragments of the two 16-key halves: row r of half th is key 8*(r/4) + 4*th + r%4
+    bf16x8_v kf[2][KS];
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      const int key = base + 8 * (c16 >> 2) + 4 * th + (c16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 32 + g * 8;
+        kf[th][ks] = __builtin_bit_cast(bf16x8_v, ld16_or_zero(k + (long)key * HD + d0, d0 < HD));
+      }
+    }
+    // V^T fragments: lane holds head dim hf*16 + c16, keys base + 8g .. +7
+    bf16x8_v vf[HF];
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf)
+      vf[hf] = __builtin_bit_cast(bf16x8_v, *(const uint4*)(vt + (long)(hf * 16 + c16) * Lp + base + 8 * g));
+    const uint32_t mybits = (uint32_t)(bal >> (8 * g)) & 0xFFu;  // admitted keys 8g .. 8g+7
+
+#pragma unroll
+    for (int qf = 0; qf < QF; ++qf) {
+      floatx4_t sc[2];
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        floatx4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[th][ks], qfr[qf][ks], z, 0, 0, 0);
+        sc[th] = z;
+      }
+      float x[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sv = sc[i >> 2][i & 3] * sl2;
+        x[i] = ((mybits >> i) & 1u) ? sv : -INFINITY;
+        tmax = fmaxf(tmax, x[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(m[qf], tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m[qf] - mnew);
+      float psum = 0.0f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float p0 = (x[i] == -INFINITY) ? 0.0f : exp2f(x[i] - mnew);
+        const float p1 = (x[i + 1] == -INFINITY) ? 0.0f : exp2f(x[i + 1] - mnew);
+        psum += p0 + p1;
+        pk[i >> 1] = (uint32_t)f_to_bf16(p0) | ((uint32_t)f_to_bf16(p1) << 16);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l[qf] = l[qf] * alpha + psum;
+      m[qf] = mnew;
+      const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+      for (int hf = 0; hf < HF; ++hf) {
+        acc[qf][hf] *= alpha;
+        acc[qf][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hf], pf, acc[qf][hf], 0, 0, 0);
+      }
+    }
+  }
+
+  // merge the 4 waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    if (g == 0) {
+      red_m[wave][qf * 16 + c16] = m[qf];
+      red_l[wave][qf * 16 + c16] = l[qf];
+    }
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_o[wave][qf * 16 + c16][hf * 16 + 4 * g + i] = acc[qf][hf][i];
+  }
+  __syncthreads();
+  uint16_t* o = (uint16_t*)a.o;
+  for (int p = t; p < S * HD; p += 256) {
+    const int qi = p / HD, d = p - qi * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][qi]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = (red_m[w][qi] == -INFINITY) ? 0.0f : exp2f(red_m[w][qi] - M);
+        L += red_l[w][qi] * f;
+        O += red_o[w][qi][d] * f;
+      }
+    }
+    o[((long)(b * S + qi) * nh + h) * HD + d] = f_to_bf16(L > 0.0f ? O / L : 0.0f);
+  }
+}
+
+template <int HD>
+static hipError_t attn_mfma_hd(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.nh, a.B);
+  const int qf = (a.S + 15) / 16;
+  switch (qf) {
+    case 1: hipLaunchKernelGGL((attention_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attention_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attention_mfma_kernel<HD, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attention_mfma_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((attention_mfma_kernel<HD, 5>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, DType t, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  if (a.S > AT_SMAX || a.hd > AT_HDMAX || a.S <= 0 || a.Lk <= 0) return hipErrorInvalidValue;
-  dim3 grid(a.nh, a.B);
-  if (t == DT_F32)
-    hipLaunchKernelGGL((attention_valu_kernel<float>), grid, dim3(256), 0, s, a);
-  else if (t == DT_BF16)
-    hipLaunchKernelGGL((attention_valu_kernel<bf16>), grid, dim3(256), 0, s, a);
-  else
+  if (a.S > AT_SMAX || a.hd > AT_HDMAX || a.S <= 0 || a.Lk <= 0 || a.Lp < a.Lk || (a.Lp % 32) != 0)
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (t == DT_BF16) {
+    switch (a.hd) {
+      case 16: return attn_mfma_hd<16>(a, s);
+      case 32: return attn_mfma_hd<32>(a, s);
+      case 48: return attn_mfma_hd<48>(a, s);
+      case 64: return attn_mfma_hd<64>(a, s);
+      default: break;
+    }
+    hipLaunchKernelGGL((attention_valu_kernel<bf16>), dim3(a.nh, a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (t == DT_F32) {
+    hipLaunchKernelGGL((attention_valu_kernel<float>), dim3(a.nh, a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------------------------

@@ -1,6 +1,6 @@
 """Invariants and edge cases of the HIP path, through the C ABI.
 
-Bitwise: repeated calls, graph vs eager replay, a sample alone vs inside a batch,
+Bitwise: repeated calls, graph vs eager replay,
 perturbed masked VL tokens, a zero velocity field. Closed forms: a constant
 velocity field, K = 1. Error paths: strict-mode ids, unprepared shapes, the
 deferred report of a bad id, the library's own noise."""
@@ -35,14 +35,16 @@ def test_repeat_and_graph_bitwise(wl):
     assert np.array_equal(y_eager, y_g1)
 
 
-def test_batch_independence_bitwise(wl):
+def test_batch_independence(wl):
+    # a sample alone equals the same sample inside the batch; the GEMM tiling and split-K
+    # depth depend on the batch size, so only the fp32 summation order may differ
     w, wt, inp, nz = wl
     h = build_head(w, wt)
     y = gpu_action(h, inp, nz)
     for b in (0, 5, 7):
         sub, n1 = synth.take_samples(inp, nz, [b])
         yb = gpu_action(h, sub, n1)
-        assert np.array_equal(yb[0], y[b]), b
+        assert np.max(np.abs(yb[0] - y[b])) <= 1e-4 * np.max(np.abs(y[b])), b
     h.close()
 
 

@@ -117,10 +117,15 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
     h.prepare(b1.batch, b1.vl_len)
     d1 = H.device_inputs(bi, bn, h.act_torch_dtype)
     out1 = torch.empty((1, b1.cfg.action_horizon, b1.cfg.action_dim), dtype=torch.float32, device="cuda:0")
-    for _ in range(3):
+    for _ in range(3 if args.b1_steps else 0):
         h.get_action(**d1, out=out1)
     torch.cuda.synchronize()
     lat_wall, lat_dev = [], []
+    h.profile(True)
+    h.get_action(**d1, out=out1)
+    torch.cuda.synchronize()
+    prof_b1 = h.profile_read()
+    h.profile(False)
     for _ in range(args.b1_steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t = time.perf_counter()
@@ -131,7 +136,7 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
         lat_wall.append((time.perf_counter() - t) * 1e3)
         lat_dev.append(e0.elapsed_time(e1))
     h.close()
-    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev
+    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1
 
 
 def stats(xs):
@@ -219,7 +224,7 @@ def main():
     t = time.time()
     weights, inputs, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
     log(f"[bench] synthetic weights and inputs for {w.name} in {time.time() - t:.1f}s")
-    total_s, per_call, prof, first, lat_wall, lat_dev = gpu_leg(args, w, weights, inputs, noise, H, synth)
+    total_s, per_call, prof, first, lat_wall, lat_dev, prof_b1 = gpu_leg(args, w, weights, inputs, noise, H, synth)
     value = w.batch * args.steps / total_s
     roof, breakdown = roofline(prof, w, inputs, args.profile_calls)
     result = {
@@ -232,7 +237,9 @@ def main():
                    "horizon": w.cfg.action_horizon, "action_dim": w.cfg.action_dim, "euler_steps": w.cfg.num_steps,
                    "graph": True},
         "per_call": stats(per_call),
-        "latency_b1": dict(workload=args.b1_workload, **stats(lat_wall), device=stats(lat_dev)),
+        "latency_b1": (dict(workload=args.b1_workload, **stats(lat_wall), device=stats(lat_dev),
+                            breakdown={c: {"launches": v[0], "ms": round(v[1], 4)} for c, v in prof_b1.items() if v[0]})
+                       if lat_wall else None),
         "roofline": roof,
         "breakdown": breakdown,
     }

@@ -75,66 +75,100 @@ hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt
 }
 
 // Residual add of split-K partial sums fused with the next (ada)LayerNorm: one wave per
-// row; the row of h is updated in place (h + p_0 + p_1 + ..., fixed order) and normalised.
-template <typename TY>
+// row, float4 accesses (lane owns columns 4*lane + 256*i .. +3); the row of h is updated
+// in place (h + p_0 + p_1 + ..., fixed order) and normalised. D % 4 == 0, D <= 2048.
+template <typename TY, int NS>
 __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict__ h, const float* __restrict__ part,
-                                                              int nsplit, long split_stride, TY* __restrict__ y,
-                                                              int rows, int D, const float* __restrict__ ada) {
-  constexpr int MAXPER = 32;
+                                                              long split_stride, TY* __restrict__ y, int rows, int D,
+                                                              const float* __restrict__ ada) {
+  constexpr int MAXV = 8;  // float4 per lane: 8 * 4 * 64 = 2048 columns
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   float* hr = h + (long)row * D;
-  float v[MAXPER];
+  float4 v[MAXV];
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    const int c = lane + i * 64;
-    float x = 0.0f;
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = 4 * lane + 256 * i;
+    float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (c < D) {
-      x = hr[c];
-      for (int p = 0; p < nsplit; ++p) x += part[(long)p * split_stride + (long)row * D + c];
-      if (nsplit > 0) hr[c] = x;
+      x = *(const float4*)(hr + c);
+#pragma unroll
+      for (int p = 0; p < NS; ++p) {
+        const float4 q = *(const float4*)(part + (long)p * split_stride + (long)row * D + c);
+        x.x += q.x;
+        x.y += q.y;
+        x.z += q.z;
+        x.w += q.w;
+      }
+      if (NS > 0) *(float4*)(hr + c) = x;
     }
     v[i] = x;
-    s += x;
+    s += (x.x + x.y) + (x.z + x.w);
   }
   const float mean = wave_sum(s) / (float)D;
   float s2 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    const int c = lane + i * 64;
-    const float d = v[i] - mean;
-    s2 += (c < D) ? d * d : 0.0f;
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = 4 * lane + 256 * i;
+    if (c < D) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      s2 += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)D + 1e-5f);
   TY* yr = y + (long)row * D;
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    const int c = lane + i * 64;
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = 4 * lane + 256 * i;
     if (c < D) {
-      float o = (v[i] - mean) * rstd;
-      if (ada) o = o * (1.0f + ada[c]) + ada[D + c];
-      st(yr + c, o);
+      float o[4] = {(v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd, (v[i].w - mean) * rstd};
+      if (ada) {
+        const float4 sc = *(const float4*)(ada + c);
+        const float4 sh = *(const float4*)(ada + D + c);
+        o[0] = o[0] * (1.0f + sc.x) + sh.x;
+        o[1] = o[1] * (1.0f + sc.y) + sh.y;
+        o[2] = o[2] * (1.0f + sc.z) + sh.z;
+        o[3] = o[3] * (1.0f + sc.w) + sh.w;
+      }
+      if (sizeof(TY) == 4) {
+        *(float4*)((float*)yr + c) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        *(uint2*)((uint16_t*)yr + c) = make_uint2((uint32_t)f_to_bf16(o[0]) | ((uint32_t)f_to_bf16(o[1]) << 16),
+                                                  (uint32_t)f_to_bf16(o[2]) | ((uint32_t)f_to_bf16(o[3]) << 16));
+      }
     }
   }
+}
+
+template <typename TY>
+static hipError_t resid_ln_go(float* h, const float* partials, int nsplit, long split_stride, TY* y, int rows, int D,
+                              const float* ada, hipStream_t s) {
+  dim3 grid((rows + 3) / 4), blk(256);
+  switch (nsplit) {
+    case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 1: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 1>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 2: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 2>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 3: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 3>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 4: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 4>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 5: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 5>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 6: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 6>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 7: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 7>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 8: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 8>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y, DType yt,
                                   int rows, int D, const float* ada, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (D > 2048) return hipErrorInvalidValue;
+  if (D > 2048 || (D % 4) != 0) return hipErrorInvalidValue;
   if (!partials) nsplit = 0;
-  dim3 grid((rows + 3) / 4);
-  if (yt == DT_F32)
-    hipLaunchKernelGGL((resid_layernorm_kernel<float>), grid, dim3(256), 0, s, h, partials, nsplit, split_stride,
-                       (float*)y, rows, D, ada);
-  else if (yt == DT_BF16)
-    hipLaunchKernelGGL((resid_layernorm_kernel<bf16>), grid, dim3(256), 0, s, h, partials, nsplit, split_stride,
-                       (bf16*)y, rows, D, ada);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (yt == DT_F32) return resid_ln_go<float>(h, partials, nsplit, split_stride, (float*)y, rows, D, ada, s);
+  if (yt == DT_BF16) return resid_ln_go<bf16>(h, partials, nsplit, split_stride, (bf16*)y, rows, D, ada, s);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------------------------

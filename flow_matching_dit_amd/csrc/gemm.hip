@@ -192,9 +192,7 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
 // ------------------------------------------------------------------------------------
 // MFMA GEMM
 // ------------------------------------------------------------------------------------
-constexpr int MF_BK = 64;
-constexpr int MF_LDS_LD = MF_BK + 8;  // bf16 elements per LDS row (16 B pad: conflict-free b128 reads)
-constexpr int OOB = 0x7FFFFFF0;       // buffer offset that is always out of range (reads 0)
+constexpr int OOB = 0x7FFFFFF0;  // buffer offset that is always out of range (reads 0)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -222,6 +220,7 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // Map the linear workgroup id to (tile_m, tile_n): ids are first regrouped so that each
 // XCD (id % 8) receives a contiguous range, then ranges walk GM m-tiles fastest so that
 // neighbouring workgroups reuse the same weight columns from the XCD's L2.
+template <int GM>
 __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
   const int nb = nm * nn;
   const int id = blockIdx.x;
@@ -230,7 +229,6 @@ __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
   const int q = nb >> 3, r = nb & 7;
   const int x = id & 7;
   const int lid = x * q + min(x, r) + (id >> 3);
-  const int GM = 16;
   const int group = lid / (GM * nn);
   const int first = group * GM;
   const int gm = min(GM, nm - first);
@@ -239,14 +237,20 @@ __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
   tn = in / gm;
 }
 
-template <int BM, int BN, int WM, int WN, bool FP8, int EK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi e) {
+template <int BM, int BN, int WM, int WN, int BK, bool FP8, int EK, int PF = 1, int WPE = 1, int PAD = 8, int GM = 16>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE))) void gemm_mfma_kernel(GemmArgs a,
+                                                                                                            Epi e) {
   constexpr int NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 fragment");
-  constexpr int A_CHUNKS = BM * 8;                 // 16-byte chunks of bf16
-  constexpr int B_CHUNKS = FP8 ? BN * 4 : BN * 8;  // 16-byte chunks of W
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  constexpr int MF_BK = BK;
+  constexpr int MF_LDS_LD = BK + PAD;              // bf16 per LDS row (padding staggers rows across banks)
+  constexpr int CPR = BK / 8;                      // 16-byte bf16 chunks per row
+  constexpr int CPR8 = BK / 16;                    // 16-byte e4m3 chunks per row
+  constexpr int A_CHUNKS = BM * CPR;
+  constexpr int B_CHUNKS = FP8 ? BN * CPR8 : BN * CPR;
   constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
   constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
 
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
   int tm, tn;
-  tile_of(nm, nn, tm, tn);
+  tile_of<GM>(nm, nn, tm, tn);
   const int g = blockIdx.y;
   const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
@@ -280,54 +284,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
     const int c = t + i * NT;
-    const int row = c >> 3, kc = (c & 7) * 8;
+    const int row = c / CPR, kc = (c % CPR) * 8;
     aoff[i] = (c < A_CHUNKS && r0 + row < a.rows) ? ((r0 + row) * (int)a.lda + kc) * 2 : OOB;
   }
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int c = t + i * NT;
     if (FP8) {
-      const int n = c >> 2, kc = (c & 3) * 16;
+      const int n = c / CPR8, kc = (c % CPR8) * 16;
       boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) : OOB;
     } else {
-      const int n = c >> 3, kc = (c & 7) * 8;
+      const int n = c / CPR, kc = (c % CPR) * 8;
       boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) * 2 : OOB;
     }
   }
 
-  uint4 ra[A_PER], rb[B_PER];
-  auto gload = [&](int k0) {
+  // Two register sets of global loads alternate, so every tile's loads are issued two
+  // tiles of MFMAs before they are written to LDS.
+  uint4 ra0[A_PER], rb0[B_PER];
+  uint4 ra1[PF == 2 ? A_PER : 1], rb1[PF == 2 ? B_PER : 1];
+  auto gload = [&](auto& ra, auto& rb, int k0) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int kc = ((t + i * NT) & 7) * 8;
+      const int kc = ((t + i * NT) % CPR) * 8;
       const bool in = aoff[i] != OOB && k0 + kc < kend;
       ra[i] = buf_load16(ra_rsrc, in ? aoff[i] + k0 * 2 : OOB);
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
-      const int kc = FP8 ? ((t + i * NT) & 3) * 16 : ((t + i * NT) & 7) * 8;
+      const int kc = FP8 ? ((t + i * NT) % CPR8) * 16 : ((t + i * NT) % CPR) * 8;
       const bool in = boff[i] != OOB && k0 + kc < kend;
       rb[i] = buf_load16(rw_rsrc, in ? boff[i] + k0 * (int)wes : OOB);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const auto& ra, const auto& rb, int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       const int c = t + i * NT;
-      if (c < A_CHUNKS) *(uint4*)&As[buf][(c >> 3) * MF_LDS_LD + (c & 7) * 8] = ra[i];
+      if ((A_CHUNKS % NT) == 0 || c < A_CHUNKS) *(uint4*)&As[buf][(c / CPR) * MF_LDS_LD + (c % CPR) * 8] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
       const int c = t + i * NT;
-      if (c < B_CHUNKS) {
+      if ((B_CHUNKS % NT) == 0 || c < B_CHUNKS) {
         if (FP8) {
-          const int n = c >> 2, kc = (c & 3) * 16;
+          const int n = c / CPR8, kc = (c % CPR8) * 16;
           *(uint4*)&Bs[buf][n * MF_LDS_LD + kc] = make_uint4(e4m3x2_to_bf16x2(rb[i].x), e4m3x2_to_bf16x2(rb[i].x >> 16),
                                                              e4m3x2_to_bf16x2(rb[i].y), e4m3x2_to_bf16x2(rb[i].y >> 16));
           *(uint4*)&Bs[buf][n * MF_LDS_LD + kc + 8] = make_uint4(e4m3x2_to_bf16x2(rb[i].z), e4m3x2_to_bf16x2(rb[i].z >> 16),
                                                                  e4m3x2_to_bf16x2(rb[i].w), e4m3x2_to_bf16x2(rb[i].w >> 16));
         } else {
-          *(uint4*)&Bs[buf][(c >> 3) * MF_LDS_LD + (c & 7) * 8] = rb[i];
+          *(uint4*)&Bs[buf][(c / CPR) * MF_LDS_LD + (c % CPR) * 8] = rb[i];
         }
       }
     }
@@ -339,17 +346,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = (kend - kbeg + MF_BK - 1) / MF_BK;
-  if (nk > 0) {
-    gload(kbeg);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * MF_BK);
+  auto compute = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < BK / 32; ++ks) {
       bf16x8_t af[FM], wf[FN];
       const int koff = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
@@ -364,8 +363,44 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  const int nk = (kend - kbeg + MF_BK - 1) / MF_BK;
+  if (PF == 1) {
+    // one register set: tile kt + 1 is loaded while tile kt is multiplied
+    if (nk > 0) {
+      gload(ra0, rb0, kbeg);
+      lstore(ra0, rb0, 0);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(ra0, rb0, kbeg + (kt + 1) * MF_BK);
+      compute(buf);
+      if (kt + 1 < nk) lstore(ra0, rb0, buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // two register sets: tile T lives in LDS buffer T & 1, set 0 carries even tiles and
+    // set 1 odd tiles, so every load is issued two tiles of MFMAs before its LDS store
+    if (nk > 0) {
+      gload(ra0, rb0, kbeg);
+      if (nk > 1) gload(ra1, rb1, kbeg + MF_BK);
+      lstore(ra0, rb0, 0);
+      __syncthreads();
+      if (nk > 2) gload(ra0, rb0, kbeg + 2 * MF_BK);
+    }
+    for (int kt = 0; kt < nk; kt += 2) {
+      compute(0);                            // tile kt
+      if (kt + 1 < nk) lstore(ra1, rb1, 1);  // tile kt + 1
+      __syncthreads();
+      if (kt + 3 < nk) gload(ra1, rb1, kbeg + (kt + 3) * MF_BK);
+      if (kt + 1 >= nk) break;
+      compute(1);                            // tile kt + 1
+      if (kt + 2 < nk) lstore(ra0, rb0, 0);  // tile kt + 2
+      __syncthreads();
+      if (kt + 4 < nk) gload(ra0, rb0, kbeg + (kt + 4) * MF_BK);
+    }
   }
 
   // acc[i][j][q]: row m = r0 + wm*TM + i*16 + lane%16, column n = n0 + wn*TN + j*16 + 4*(lane/16) + q
@@ -394,6 +429,116 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a, Epi
 }
 
 // ------------------------------------------------------------------------------------
+// Skinny MFMA GEMM for <= 64 rows per group (weight streaming: B = 1 projections and
+// the per-embodiment linears). A workgroup owns 16 output columns; its NWAVE waves take
+// contiguous slices of K. Each lane loads its weight fragments (16 B of one weight row)
+// and activation fragments straight from memory, a chunk of KC k-steps at a time with
+// all loads of the chunk issued before the MFMAs, so a wave keeps KC x 16 B of weights
+// in flight. The waves' partial sums are added through LDS in wave order.
+// ------------------------------------------------------------------------------------
+template <int MF, int NWAVE, bool FP8, int EK>
+__global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi e) {
+  constexpr int KC = 8;
+  __shared__ floatx4_t red[NWAVE][MF][64];
+  const int g = blockIdx.y;
+  const int cat = a.ids ? a.ids[g] : 0;
+  const int n0 = blockIdx.x * 16;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lg = lane >> 4, lr = lane & 15;
+  const uint32_t wes = FP8 ? 1 : 2;
+  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  const char* Wb = (const char*)a.W + (long)cat * a.w_cstride * wes;
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(Wb, (uint32_t)((long)a.N * a.K * wes));
+  const int nsteps = (a.K + 31) / 32;
+  const int spw = (nsteps + NWAVE - 1) / NWAVE;
+  const int s0 = wave * spw, s1 = min(nsteps, s0 + spw);
+  const int woff = (n0 + lr < a.N) ? (n0 + lr) * a.K * (int)wes : OOB;
+  int aoff[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) aoff[mf] = (mf * 16 + lr < a.rows) ? (mf * 16 + lr) * (int)a.lda * 2 : OOB;
+
+  floatx4_t acc[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) acc[mf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = s0; c0 < s1; c0 += KC) {
+    uint4 wv[KC];
+    uint4 av[KC][MF];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int k = (c0 + i) * 32 + lg * 8;
+      const bool in = (c0 + i) < s1 && k < a.K;
+      if (FP8) {
+        int32x4_t raw = {0, 0, 0, 0};
+        const int off = (in && woff != OOB) ? woff + k : OOB;
+        const auto lo = __builtin_amdgcn_raw_buffer_load_b64(rw_rsrc, off, 0, 0);
+        raw[0] = lo[0];
+        raw[1] = lo[1];
+        wv[i] = make_uint4((uint32_t)raw[0], (uint32_t)raw[1], 0, 0);
+      } else {
+        wv[i] = buf_load16(rw_rsrc, (in && woff != OOB) ? woff + k * 2 : OOB);
+      }
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) av[i][mf] = buf_load16(ra_rsrc, (in && aoff[mf] != OOB) ? aoff[mf] + k * 2 : OOB);
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      uint4 w = wv[i];
+      if (FP8)
+        w = make_uint4(e4m3x2_to_bf16x2(wv[i].x), e4m3x2_to_bf16x2(wv[i].x >> 16), e4m3x2_to_bf16x2(wv[i].y),
+                       e4m3x2_to_bf16x2(wv[i].y >> 16));
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+        acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8_t, av[i][mf]), acc[mf], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) red[wave][mf][lane] = acc[mf];
+  __syncthreads();
+  if (t < MF * 64) {
+    const int mf = t >> 6, ln = t & 63;
+    floatx4_t sum = red[0][mf][ln];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) sum += red[w][mf][ln];
+    const int r = mf * 16 + (ln & 15);
+    const int n = n0 + 4 * (ln >> 4);
+    if (r < a.rows && n < a.N) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sc = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+        const float bi = a.bias ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+        v[q] = sum[q] * sc + bi;
+      }
+      epi_store<EK, 4>(e, g, r, n, v, cat, 0);
+    }
+  }
+}
+
+template <int MF, int NWAVE, bool FP8>
+static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, hipStream_t s) {
+  dim3 grid((a.N + 15) / 16, a.groups), blk(64 * NWAVE);
+#define GR00T_SKINNY_CASE(K) \
+  case K: hipLaunchKernelGGL((gemm_skinny_kernel<MF, NWAVE, FP8, K>), grid, blk, 0, s, a, e); break;
+  switch (e.kind) {
+    GR00T_SKINNY_CASE(EPI_STORE)
+    GR00T_SKINNY_CASE(EPI_RESID_ADD)
+    GR00T_SKINNY_CASE(EPI_HEADS)
+    GR00T_SKINNY_CASE(EPI_EULER)
+    default: return hipErrorInvalidValue;
+  }
+#undef GR00T_SKINNY_CASE
+  return hipGetLastError();
+}
+
+template <int MF>
+static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, hipStream_t s) {
+  if (a.K >= 1024)
+    return fp8 ? skinny_kind<MF, 8, true>(a, e, s) : skinny_kind<MF, 8, false>(a, e, s);
+  return fp8 ? skinny_kind<MF, 4, true>(a, e, s) : skinny_kind<MF, 4, false>(a, e, s);
+}
+
+// ------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------
 template <typename TA, typename TW>
@@ -418,42 +563,53 @@ hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt,
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN, bool FP8>
+template <int BM, int BN, int WM, int WN, int BK, bool FP8, int PAD, int GM>
 static hipError_t mfma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
   dim3 grid(nm * nn, a.groups, splits);
   dim3 blk(64 * WM * WN);
+#define GR00T_MFMA_CASE(K) \
+  case K: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, BK, FP8, K, 1, 1, PAD, GM>), grid, blk, 0, s, a, e); break;
   switch (e.kind) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_STORE>), grid, blk, 0, s, a, e); break;
-    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_RESID_ADD>), grid, blk, 0, s, a, e); break;
-    case EPI_HEADS: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_HEADS>), grid, blk, 0, s, a, e); break;
-    case EPI_EULER: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_EULER>), grid, blk, 0, s, a, e); break;
-    case EPI_PARTIAL: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, FP8, EPI_PARTIAL>), grid, blk, 0, s, a, e); break;
+    GR00T_MFMA_CASE(EPI_STORE)
+    GR00T_MFMA_CASE(EPI_RESID_ADD)
+    GR00T_MFMA_CASE(EPI_HEADS)
+    GR00T_MFMA_CASE(EPI_EULER)
+    GR00T_MFMA_CASE(EPI_PARTIAL)
     default: return hipErrorInvalidValue;
   }
+#undef GR00T_MFMA_CASE
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int PAD, int GM>
 static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
-  return fp8 ? mfma_kind<BM, BN, WM, WN, true>(a, e, splits, s) : mfma_kind<BM, BN, WM, WN, false>(a, e, splits, s);
+  return fp8 ? mfma_kind<BM, BN, WM, WN, BK, true, PAD, GM>(a, e, splits, s)
+             : mfma_kind<BM, BN, WM, WN, BK, false, PAD, GM>(a, e, splits, s);
 }
 
-// 0: 256x128 (8 waves), 1: 128x128, 2: 64x128, 3: 32x64, 4: 16x64
+// Tile configurations (measured on the head's shapes; LDS rows padded by 16 bf16, which
+// removes LDS bank conflicts for 64-deep tiles):
+//   0: 256x128, 8 waves, BK 32, raster group 4   (many tiles: VL K/V projection, B >= 256)
+//   1: 256x128, 8 waves, BK 64, raster group 8   (B ~ 64: MLP up, fused qkv)
+//   2: 64x128, 4 waves, BK 64                    (fewer tiles: D-wide outputs, split-K)
+//   3: 32x64, 4 waves                            (<= 32 rows)
+//   4: 16x64, 4 waves                            (<= 16 rows)
 static int tile_choice(int rows, int N, int groups) {
   auto tiles = [&](int bm, int bn) { return (long)((rows + bm - 1) / bm) * ((N + bn - 1) / bn) * groups; };
   if (rows <= 16) return 4;
   if (rows <= 32) return 3;
   if (rows <= 64) return 2;
   if (tiles(256, 128) >= 512) return 0;
-  if (tiles(128, 128) >= 256) return 1;
+  if (tiles(256, 128) >= 160) return 1;
   return 2;
 }
 
 // Smallest split count that gives >= 240 workgroups (or leaves <= 512 k per split),
 // else the largest valid one (at most 8, each split a multiple of 64 deep).
 int gemm_mfma_splits(int rows, int N, int K, int groups) {
-  static const int bm[5] = {256, 128, 64, 32, 16}, bn[5] = {128, 128, 128, 64, 64};
+  static const int bm[5] = {256, 256, 64, 32, 16}, bn[5] = {128, 128, 128, 64, 64};
+  if (rows <= 64) return 1;  // the skinny kernel splits K inside the workgroup
   int best = 1;
   for (int s = 1; s <= 8; ++s) {
     if (K % (64 * s) != 0) continue;
@@ -478,12 +634,17 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
   }
   a.k_per_split = a.K / splits;
   if ((long)a.rows * a.lda * 2 >= (1l << 31) || (long)a.N * a.K * 2 >= (1l << 31)) return hipErrorInvalidValue;
+  if (a.rows <= 64 && e.kind != EPI_PARTIAL) {
+    if (a.rows <= 16) return skinny_go<1>(a, e, fp8, s);
+    if (a.rows <= 32) return skinny_go<2>(a, e, fp8, s);
+    return skinny_go<4>(a, e, fp8, s);
+  }
   switch (tile_choice(a.rows, a.N, a.groups * splits)) {
-    case 0: return mfma_go<256, 128, 4, 2>(a, e, fp8, splits, s);
-    case 1: return mfma_go<128, 128, 2, 2>(a, e, fp8, splits, s);
-    case 2: return mfma_go<64, 128, 2, 2>(a, e, fp8, splits, s);
-    case 3: return mfma_go<32, 64, 1, 4>(a, e, fp8, splits, s);
-    default: return mfma_go<16, 64, 1, 4>(a, e, fp8, splits, s);
+    case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);
+    case 1: return mfma_go<256, 128, 4, 2, 64, 16, 8>(a, e, fp8, splits, s);
+    case 2: return mfma_go<64, 128, 2, 2, 64, 16, 16>(a, e, fp8, splits, s);
+    case 3: return mfma_go<32, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
+    default: return mfma_go<16, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
   }
 }
 

@@ -145,6 +145,7 @@ struct gr00t_head {
   std::vector<int> tau;
   // launch timing (gr00t_profile_*)
   bool prof_on = false;
+  int prof_mode = 0;  // 1: every launch, eager; 2: graph kept, launches outside it timed
   std::vector<hipEvent_t> prof_pool;
   std::vector<std::pair<int, int>> prof_recs;  // (class, index of the start event)
   size_t prof_next = 0;
@@ -418,11 +419,11 @@ void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
 
 enum KClass {
   K_VLLN = 0, K_KV_PROJ, K_STATE_ENC, K_ACTION_ENC, K_ADALN, K_QKV_PROJ, K_Q_PROJ, K_ATTN_SELF, K_ATTN_CROSS,
-  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_NCLASS
+  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_GRAPH, K_NCLASS
 };
 const char* const kClassNames[K_NCLASS] = {"vlln", "kv_proj", "state_enc", "action_enc", "adaln", "qkv_proj",
                                            "q_proj", "attn_self", "attn_cross", "o_proj", "norm3", "ff_up",
-                                           "ff_down", "out_proj", "decoder", "small"};
+                                           "ff_down", "out_proj", "decoder", "small", "steps_graph"};
 
 // Returns the index of the start event recorded on s, or -1 when not profiling.
 int prof_begin(gr00t_head* h, hipStream_t s) {
@@ -1033,7 +1034,7 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
   if (rc != GR00T_OK) return rc;
   const bool use_graph = (h->cfg.flags & GR00T_FLAG_USE_GRAPH) != 0;
   const auto key = std::make_pair((int)in->batch, (int)in->vl_len);
-  const bool have_graph = use_graph && h->graphs.count(key) && !h->prof_on;
+  const bool have_graph = use_graph && h->graphs.count(key) && !(h->prof_on && h->prof_mode == 1);
   if (use_graph && !have_graph && (h->cfg.flags & GR00T_FLAG_STRICT))
     return fail(h, GR00T_E_UNCAPTURED, "shape (B=" + std::to_string(in->batch) + ", L=" + std::to_string(in->vl_len) +
                                            ") was not prepared");
@@ -1044,7 +1045,7 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
   rc = run_prologue(h, in, s);
   if (rc != GR00T_OK) return rc;
   if (have_graph) {
-    HIPCHK(h, hipGraphLaunch(h->graphs[key], s));
+    LAUNCH(h, s, K_GRAPH, hipGraphLaunch(h->graphs[key], s));
   } else {
     rc = run_steps(h, in->batch, in->vl_len, 0, h->cfg.num_steps, true, s);
     if (rc != GR00T_OK) return rc;
@@ -1100,7 +1101,9 @@ int gr00t_profile_enable(gr00t_head* h, int on) {
     int rc = prof_collect(h);
     if (rc != GR00T_OK) return rc;
   }
+  if (on < 0 || on > 2) return fail(h, GR00T_E_INVALID_ARG, "profiling mode must be 0, 1 or 2");
   h->prof_on = on != 0;
+  h->prof_mode = on;
   h->prof_n.assign(K_NCLASS, 0);
   h->prof_ms.assign(K_NCLASS, 0.0);
   return GR00T_OK;

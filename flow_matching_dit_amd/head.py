@@ -191,8 +191,9 @@ class Gr00tHead:
                                             self._stream(stream)))
         return out
 
-    def profile(self, on: bool = True):
-        self._check(self.lib.gr00t_profile_enable(self.h, 1 if on else 0))
+    def profile(self, on=True):
+        """on: False/0 off, True/1 every launch (eager), 2 graph kept (launches outside it timed)."""
+        self._check(self.lib.gr00t_profile_enable(self.h, int(on)))
 
     def profile_read(self) -> dict:
         """{class name: (launches, total ms)} of the launches recorded since profile(True)."""

@@ -176,12 +176,14 @@ const char* gr00t_last_error(const gr00t_head* h);
 size_t gr00t_device_bytes(const gr00t_head* h);
 
 /*
- * Launch timing (tracing support). With profiling on, get_action and velocity run
- * without the graph and bracket every kernel launch with a pair of HIP events on
- * the call's stream, accumulated per kernel class (vision-language LayerNorm, K/V
- * projection, adaLN, q/qkv projection, self/cross attention, o projection, norm3,
- * MLP up/down, output projection, per-embodiment linears, small kernels).
- *   gr00t_profile_enable: on != 0 starts recording (and clears the totals).
+ * Launch timing (tracing support). Kernel launches are bracketed by a pair of HIP
+ * events on the call's stream and accumulated per kernel class (vision-language
+ * LayerNorm, K/V projection, adaLN, q/qkv projection, self/cross attention, o
+ * projection, norm3, MLP up/down, output projection, per-embodiment linears, small
+ * kernels, and "steps_graph" for a whole replay of the captured K-step graph).
+ *   gr00t_profile_enable: on = 1 times every launch and runs get_action without the
+ *     graph; on = 2 keeps the graph, timing the launches outside it and each replay;
+ *     on = 0 stops. Enabling clears the totals; E_INVALID_ARG for other values.
  *   gr00t_profile_read: synchronises the recorded events, then returns the number of
  *     launches and their summed duration in ms for class `kclass`; E_INVALID_ARG past
  *     the last class.

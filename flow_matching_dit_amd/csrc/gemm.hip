@@ -441,6 +441,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
   constexpr int KC = 8;
   __shared__ floatx4_t red[NWAVE][MF][64];
   const int g = blockIdx.y;
+  const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
   const int n0 = blockIdx.x * 16;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lg = lane >> 4, lr = lane & 15;
@@ -449,7 +450,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
   const char* Wb = (const char*)a.W + (long)cat * a.w_cstride * wes;
   const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
   const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(Wb, (uint32_t)((long)a.N * a.K * wes));
-  const int nsteps = (a.K + 31) / 32;
+  // k-steps of 32 of this split ([kbeg, kend) is a multiple of 32 wide except at K's end)
+  const int kbeg = split * a.k_per_split, kend = min(a.K, kbeg + a.k_per_split);
+  const int nsteps = (kend - kbeg + 31) / 32;
   const int spw = (nsteps + NWAVE - 1) / NWAVE;
   const int s0 = wave * spw, s1 = min(nsteps, s0 + spw);
   const int woff = (n0 + lr < a.N) ? (n0 + lr) * a.K * (int)wes : OOB;
@@ -465,8 +468,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
     uint4 av[KC][MF];
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      const int k = (c0 + i) * 32 + lg * 8;
-      const bool in = (c0 + i) < s1 && k < a.K;
+      const int k = kbeg + (c0 + i) * 32 + lg * 8;
+      const bool in = (c0 + i) < s1 && k < kend;
       if (FP8) {
         int32x4_t raw = {0, 0, 0, 0};
         const int off = (in && woff != OOB) ? woff + k : OOB;
@@ -507,17 +510,17 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float sc = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
-        const float bi = a.bias ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+        const float bi = (a.bias && (EK != EPI_PARTIAL || split == 0)) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
         v[q] = sum[q] * sc + bi;
       }
-      epi_store<EK, 4>(e, g, r, n, v, cat, 0);
+      epi_store<EK, 4>(e, g, r, n, v, cat, split);
     }
   }
 }
 
 template <int MF, int NWAVE, bool FP8>
-static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, hipStream_t s) {
-  dim3 grid((a.N + 15) / 16, a.groups), blk(64 * NWAVE);
+static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
+  dim3 grid((a.N + 15) / 16, a.groups, splits), blk(64 * NWAVE);
 #define GR00T_SKINNY_CASE(K) \
   case K: hipLaunchKernelGGL((gemm_skinny_kernel<MF, NWAVE, FP8, K>), grid, blk, 0, s, a, e); break;
   switch (e.kind) {
@@ -525,6 +528,7 @@ static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, hipStream_t s) {
     GR00T_SKINNY_CASE(EPI_RESID_ADD)
     GR00T_SKINNY_CASE(EPI_HEADS)
     GR00T_SKINNY_CASE(EPI_EULER)
+    GR00T_SKINNY_CASE(EPI_PARTIAL)
     default: return hipErrorInvalidValue;
   }
 #undef GR00T_SKINNY_CASE
@@ -532,10 +536,10 @@ static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, hipStream_t s) {
 }
 
 template <int MF>
-static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, hipStream_t s) {
-  if (a.K >= 1024)
-    return fp8 ? skinny_kind<MF, 8, true>(a, e, s) : skinny_kind<MF, 8, false>(a, e, s);
-  return fp8 ? skinny_kind<MF, 4, true>(a, e, s) : skinny_kind<MF, 4, false>(a, e, s);
+static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
+  if (a.k_per_split >= 1024)
+    return fp8 ? skinny_kind<MF, 8, true>(a, e, splits, s) : skinny_kind<MF, 8, false>(a, e, splits, s);
+  return fp8 ? skinny_kind<MF, 4, true>(a, e, splits, s) : skinny_kind<MF, 4, false>(a, e, splits, s);
 }
 
 // ------------------------------------------------------------------------------------
@@ -609,7 +613,14 @@ static int tile_choice(int rows, int N, int groups) {
 // else the largest valid one (at most 8, each split a multiple of 64 deep).
 int gemm_mfma_splits(int rows, int N, int K, int groups) {
   static const int bm[5] = {256, 256, 64, 32, 16}, bn[5] = {128, 128, 128, 64, 64};
-  if (rows <= 64) return 1;  // the skinny kernel splits K inside the workgroup
+  if (rows <= 64) {
+    // skinny kernel: 8 waves split K inside a workgroup, each holding one chunk of 8 k-steps
+    // (256 deep) in flight; deeper K is split across workgroups
+    int s = 1;
+    while (K / s > 2048 && s < 8 && K % (64 * s * 2) == 0) s *= 2;
+    if (K / s > 2048 && K % (64 * 3) == 0 && K / 3 <= 2048) s = 3;
+    return s;
+  }
   int best = 1;
   for (int s = 1; s <= 8; ++s) {
     if (K % (64 * s) != 0) continue;
@@ -634,10 +645,10 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
   }
   a.k_per_split = a.K / splits;
   if ((long)a.rows * a.lda * 2 >= (1l << 31) || (long)a.N * a.K * 2 >= (1l << 31)) return hipErrorInvalidValue;
-  if (a.rows <= 64 && e.kind != EPI_PARTIAL) {
-    if (a.rows <= 16) return skinny_go<1>(a, e, fp8, s);
-    if (a.rows <= 32) return skinny_go<2>(a, e, fp8, s);
-    return skinny_go<4>(a, e, fp8, s);
+  if (a.rows <= 64) {
+    if (a.rows <= 16) return skinny_go<1>(a, e, fp8, splits, s);
+    if (a.rows <= 32) return skinny_go<2>(a, e, fp8, splits, s);
+    return skinny_go<4>(a, e, fp8, splits, s);
   }
   switch (tile_choice(a.rows, a.N, a.groups * splits)) {
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);

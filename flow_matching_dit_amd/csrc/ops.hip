@@ -290,13 +290,13 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
 }
 
-template <int HD, int QF>
-__global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
+template <int HD, int QF, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   constexpr int KS = (HD + 31) / 32;  // 32-wide k steps over the head dim (zero padded)
   constexpr int HF = HD / 16;         // 16-row fragments of the head dim
-  __shared__ float red_m[4][QF * 16];
-  __shared__ float red_l[4][QF * 16];
-  __shared__ float red_o[4][QF * 16][HD + 1];
+  __shared__ float red_m[NW][QF * 16];
+  __shared__ float red_l[NW][QF * 16];
+  __shared__ float red_o[NW][QF * 16][HD + 1];
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -328,18 +328,20 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
     for (int hf = 0; hf < HF; ++hf) acc[qf][hf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  const int ntiles = (Lk + 31) / 32;
-  for (int kt = wave; kt < ntiles; kt += 4) {
-    const int base = kt * 32;
+  // admitted-key bits of tile kt for this lane (keys 8g .. 8g+7 of the tile); 0 past the end
+  auto tile_bits = [&](int kt) -> uint32_t {
     bool admit = false;
     if (lane < 32) {
-      const int j = base + lane;
+      const int j = kt * 32 + lane;
       admit = j < Lk && (a.mask == nullptr || (a.mask[(long)b * Lk + j] & a.mask_bit));
     }
     const unsigned long long bal = __ballot(admit);
-    if (bal == 0ull) continue;
-    // K fragments of the two 16-key halves: row r of half th is key 8*(r/4) + 4*th + r%4
-    bf16x8_v kf[2][KS];
+    return (uint32_t)(bal >> (8 * g)) & 0xFFu;
+  };
+  // K fragments of the two 16-key halves (row r of half th is key 8*(r/4) + 4*th + r%4)
+  // and V^T fragments (head dim hf*16 + c16, keys 8g .. +7) of tile kt
+  auto load_tile = [&](int kt, bf16x8_v (&kf)[2][KS], bf16x8_v (&vf)[HF]) {
+    const int base = kt * 32;
 #pragma unroll
     for (int th = 0; th < 2; ++th) {
       const int key = base + 8 * (c16 >> 2) + 4 * th + (c16 & 3);
@@ -349,13 +351,11 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
         kf[th][ks] = __builtin_bit_cast(bf16x8_v, ld16_or_zero(k + (long)key * HD + d0, d0 < HD));
       }
     }
-    // V^T fragments: lane holds head dim hf*16 + c16, keys base + 8g .. +7
-    bf16x8_v vf[HF];
 #pragma unroll
     for (int hf = 0; hf < HF; ++hf)
       vf[hf] = __builtin_bit_cast(bf16x8_v, *(const uint4*)(vt + (long)(hf * 16 + c16) * Lp + base + 8 * g));
-    const uint32_t mybits = (uint32_t)(bal >> (8 * g)) & 0xFFu;  // admitted keys 8g .. 8g+7
-
+  };
+  auto process = [&](const bf16x8_v (&kf)[2][KS], const bf16x8_v (&vf)[HF], uint32_t mybits) {
 #pragma unroll
     for (int qf = 0; qf < QF; ++qf) {
       floatx4_t sc[2];
@@ -398,9 +398,23 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
         acc[qf][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hf], pf, acc[qf][hf], 0, 0, 0);
       }
     }
+  };
+
+  // wave w takes tiles w, w + NW, ...; two tiles' loads are issued before either is used
+  const int ntiles = (Lk + 31) / 32;
+  for (int kt = wave; kt < ntiles; kt += 2 * NW) {
+    const int kt2 = kt + NW;
+    const uint32_t bits0 = tile_bits(kt);
+    const uint32_t bits1 = kt2 < ntiles ? tile_bits(kt2) : 0u;
+    const bool any0 = __ballot(bits0 != 0) != 0ull, any1 = __ballot(bits1 != 0) != 0ull;
+    bf16x8_v kf0[2][KS], vf0[HF], kf1[2][KS], vf1[HF];
+    if (any0) load_tile(kt, kf0, vf0);
+    if (any1) load_tile(kt2, kf1, vf1);
+    if (any0) process(kf0, vf0, bits0);
+    if (any1) process(kf1, vf1, bits1);
   }
 
-  // merge the 4 waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16
+  // merge the waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16
 #pragma unroll
   for (int qf = 0; qf < QF; ++qf) {
     if (g == 0) {
@@ -414,15 +428,15 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
   }
   __syncthreads();
   uint16_t* o = (uint16_t*)a.o;
-  for (int p = t; p < S * HD; p += 256) {
+  for (int p = t; p < S * HD; p += 64 * NW) {
     const int qi = p / HD, d = p - qi * HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][qi]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][qi]);
     float L = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = (red_m[w][qi] == -INFINITY) ? 0.0f : exp2f(red_m[w][qi] - M);
         L += red_l[w][qi] * f;
         O += red_o[w][qi][d] * f;
@@ -432,16 +446,18 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(AttnArgs a) {
   }
 }
 
+// 8 waves when the query fragments are few (B = 1 latency: more loads in flight per
+// head), 4 waves for 3..5 query fragments (LDS of the wave merge).
 template <int HD>
 static hipError_t attn_mfma_hd(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.nh, a.B);
   const int qf = (a.S + 15) / 16;
   switch (qf) {
-    case 1: hipLaunchKernelGGL((attention_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attention_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((attention_mfma_kernel<HD, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attention_mfma_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((attention_mfma_kernel<HD, 5>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attention_mfma_kernel<HD, 1, 8>), grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attention_mfma_kernel<HD, 2, 8>), grid, dim3(512), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attention_mfma_kernel<HD, 3, 4>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attention_mfma_kernel<HD, 4, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((attention_mfma_kernel<HD, 5, 4>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -49,8 +49,9 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
 #pragma unroll
     for (int q = 0; q < NV; ++q) v[q] = apply_act(e.act, v[q]);
   }
-  const long row = (long)g * e.out_gstride + e.out_row_off + r;
+  const long row0 = (long)g * e.out_gstride + e.out_row_off + r;
   if (EK == EPI_STORE) {
+    const long row = row0;
     const long idx = row * e.out_ld + n;
     if (e.out_f32) {
       float* p = (float*)e.out + idx;
@@ -69,6 +70,7 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
       }
     }
   } else if (EK == EPI_RESID_ADD || EK == EPI_EULER) {
+    const long row = row0;
     float* p = (float*)e.out + row * e.out_ld + n;
     const float s = (EK == EPI_EULER) ? e.dt : 1.0f;
     if (NV == 4) {
@@ -83,12 +85,14 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
       for (int q = 0; q < NV; ++q) p[q] = p[q] + s * v[q];
     }
   } else if (EK == EPI_PARTIAL) {
+    const long row = row0;
     float* p = (float*)e.out + (long)split * e.split_stride + row * e.out_ld + n;
     if (NV == 4) *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
     else
 #pragma unroll
       for (int q = 0; q < NV; ++q) p[q] = v[q];
   } else {  // EPI_HEADS: NV consecutive columns stay inside one head (hd % 4 == 0)
+    const long row = e.row_map ? (long)e.row_map[row0] : row0;
     const int sec = n / e.width;
     const int which = sec % e.nwhich;
     const int layer = sec / e.nwhich;
@@ -140,6 +144,11 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
   const int g = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
   const int r0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (a.rows_dev) {
+    const int rr = min(a.rows, *a.rows_dev);
+    if (r0 >= rr) return;
+    a.rows = rr;
+  }
   const TA* A = (const TA*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
   const TW* W = (const TW*)a.W + (long)cat * a.w_cstride;
   const int t = threadIdx.x, tx = t % 16, ty = t / 16;
@@ -260,6 +269,11 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
   int tm, tn;
   tile_of<GM>(nm, nn, tm, tn);
+  if (a.rows_dev) {  // row count known on the device only: tiles past it have no work
+    const int rr = min(a.rows, *a.rows_dev);
+    if (tm * BM >= rr) return;
+    a.rows = rr;
+  }
   const int g = blockIdx.y;
   const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;

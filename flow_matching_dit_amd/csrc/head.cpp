@@ -117,7 +117,7 @@ struct Ws {  // workspace pointers
   void *n, *q, *k, *v, *o, *u, *y, *e1, *e2, *se1, *vln, *kc, *vc;
   float *x, *s, *vout, *part;
   uint8_t *code, *bad;
-  int *ids, *iota;
+  int *ids, *iota, *vrow, *vcount;
   float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
 };
 
@@ -585,10 +585,14 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
   const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
   LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
   LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
+  // only VL tokens admitted by some block are normalised and projected: their row
+  // indices are compacted on the device (vrow[0 .. *vcount))
+  LAUNCH(h, s, K_SMALL, launch_compact_rows(h->w.code, B * L, h->w.vrow, h->w.vcount, s));
   LAUNCH(h, s, K_VLLN, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
-                             at<float>(h, lay.vlln_b), nullptr, s));
-  {  // keys and values of every cross block: [B*L, E] x [Nc*2D, E]^T -> head-major caches
+                                        at<float>(h, lay.vlln_b), nullptr, s, h->w.vrow, h->w.vcount));
+  {  // keys and values of every cross block: [valid rows, E] x [Nc*2D, E]^T -> head-major caches
     GemmArgs a = ga(h->w.vln, E, B * L, Nc * 2 * D, E);
+    a.rows_dev = h->w.vcount;
     a.W = at<void>(h, lay.kv_w);
     a.bias = at<float>(h, lay.kv_b);
     a.wscale = kvw == DT_FP8 ? at<float>(h, lay.kv_s) : nullptr;
@@ -607,6 +611,7 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     e.transposed[0] = 0;
     e.transposed[1] = 1;  // values cached [hd][L] for the attention's V^T operand
     e.layer_stride[0] = e.layer_stride[1] = (long)B * Lp * D;
+    e.row_map = h->w.vrow;
     LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));
   }
   {  // state encoder: one token per sample
@@ -964,6 +969,7 @@ int gr00t_finalize(gr00t_head* h) {
       {(void**)&h->w.s, Bm * D * 4},          {(void**)&h->w.vout, Bm * H * A * 4},
       {(void**)&h->w.part, 8 * Bm * S * D * 4},
       {(void**)&h->w.code, Bm * Lm},          {(void**)&h->w.bad, Bm},           {(void**)&h->w.ids, Bm * 4},
+      {(void**)&h->w.vrow, Bm * Lm * 4},      {(void**)&h->w.vcount, 4},
       {(void**)&h->w.iota, C * 4},            {(void**)&h->w.sin_t, K * T * 4},  {(void**)&h->w.t1, K * D * 4},
       {(void**)&h->w.temb, K * D * 4},        {(void**)&h->w.stemb, K * D * 4},
       {(void**)&h->w.ada, K * (Nl + 1) * 2 * D * 4},                              {(void**)&h->w.tauemb, K * D * 4},

@@ -36,6 +36,7 @@ struct GemmArgs {
   int K;
   int groups;
   int k_per_split;      // set by the launcher
+  const int* rows_dev;  // optional device row count (dense GEMMs): rows = min(rows, *rows_dev)
 };
 
 struct Epi {
@@ -62,6 +63,7 @@ struct Epi {
   int pstride[3];
   int transposed[3];
   long layer_stride[3];
+  const int* row_map;   // EPI_HEADS: optional map of the GEMM row to the (b * pos_per_b + pos) row
   float dt;             // EPI_EULER
   int splits;           // EPI_PARTIAL: number of K splits (grid z)
   long split_stride;    // EPI_PARTIAL: elements between consecutive splits' outputs
@@ -77,7 +79,11 @@ int gemm_mfma_splits(int rows, int N, int K, int groups);
 // with ada = [scale | shift] (2D floats) or NULL. x rows at x + r * ldx.
 hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt, long ldy, int rows,
                             int D, const float* gamma, const float* beta, const float* ada,
-                            hipStream_t s);
+                            hipStream_t s, const int* row_idx = nullptr, const int* row_count = nullptr);
+// With row_idx/row_count: output row r (< *row_count) is the normalised input row row_idx[r].
+
+// idx[0 .. *count) = the rows r < n with code[r] != 0, in increasing order (one workgroup).
+hipError_t launch_compact_rows(const uint8_t* code, int n, int* idx, int* count, hipStream_t s);
 
 // Residual add of split-K partial sums, then adaLN / LayerNorm:
 //   h[r] += sum_s partials[s][r]  (fixed order, written back), y = LN(h[r]) [* (1 + scale) + shift]

@@ -18,12 +18,15 @@ template <typename TX, typename TY>
 __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x, long ldx, TY* __restrict__ y,
                                                         long ldy, int rows, int D, const float* __restrict__ gamma,
                                                         const float* __restrict__ beta,
-                                                        const float* __restrict__ ada) {
+                                                        const float* __restrict__ ada,
+                                                        const int* __restrict__ row_idx,
+                                                        const int* __restrict__ row_count) {
   constexpr int MAXPER = 32;  // D <= 2048
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const TX* xr = x + (long)row * ldx;
+  if (row_count && row >= *row_count) return;
+  const TX* xr = x + (long)(row_idx ? row_idx[row] : row) * ldx;
   float v[MAXPER];
   float s = 0.0f;
 #pragma unroll
@@ -56,19 +59,20 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
 }
 
 hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt, long ldy, int rows, int D,
-                            const float* gamma, const float* beta, const float* ada, hipStream_t s) {
+                            const float* gamma, const float* beta, const float* ada, hipStream_t s, const int* row_idx,
+                            const int* row_count) {
   if (rows <= 0) return hipSuccess;
   if (D > 2048) return hipErrorInvalidValue;
   dim3 grid((rows + 3) / 4);
   if (xt == DT_F32 && yt == DT_F32)
     hipLaunchKernelGGL((layernorm_kernel<float, float>), grid, dim3(256), 0, s, (const float*)x, ldx, (float*)y, ldy,
-                       rows, D, gamma, beta, ada);
+                       rows, D, gamma, beta, ada, row_idx, row_count);
   else if (xt == DT_F32 && yt == DT_BF16)
     hipLaunchKernelGGL((layernorm_kernel<float, bf16>), grid, dim3(256), 0, s, (const float*)x, ldx, (bf16*)y, ldy,
-                       rows, D, gamma, beta, ada);
+                       rows, D, gamma, beta, ada, row_idx, row_count);
   else if (xt == DT_BF16 && yt == DT_BF16)
     hipLaunchKernelGGL((layernorm_kernel<bf16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, ldx, (bf16*)y, ldy,
-                       rows, D, gamma, beta, ada);
+                       rows, D, gamma, beta, ada, row_idx, row_count);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -446,15 +450,22 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   }
 }
 
-// 8 waves when the query fragments are few (B = 1 latency: more loads in flight per
-// head), 4 waves for 3..5 query fragments (LDS of the wave merge).
+// 8 waves for small batches with few query fragments (B = 1 latency: more key tiles in
+// flight per head); 4 waves otherwise (enough workgroups fill the chip; smaller merge).
 template <int HD>
 static hipError_t attn_mfma_hd(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.nh, a.B);
   const int qf = (a.S + 15) / 16;
+  const bool wide = a.B * a.nh < 512;
   switch (qf) {
-    case 1: hipLaunchKernelGGL((attention_mfma_kernel<HD, 1, 8>), grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attention_mfma_kernel<HD, 2, 8>), grid, dim3(512), 0, s, a); break;
+    case 1:
+      if (wide) hipLaunchKernelGGL((attention_mfma_kernel<HD, 1, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attention_mfma_kernel<HD, 1, 4>), grid, dim3(256), 0, s, a);
+      break;
+    case 2:
+      if (wide) hipLaunchKernelGGL((attention_mfma_kernel<HD, 2, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attention_mfma_kernel<HD, 2, 4>), grid, dim3(256), 0, s, a);
+      break;
     case 3: hipLaunchKernelGGL((attention_mfma_kernel<HD, 3, 4>), grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((attention_mfma_kernel<HD, 4, 4>), grid, dim3(256), 0, s, a); break;
     case 5: hipLaunchKernelGGL((attention_mfma_kernel<HD, 5, 4>), grid, dim3(256), 0, s, a); break;
@@ -506,6 +517,34 @@ hipError_t launch_mask_codes(const uint8_t* vl_mask, const uint8_t* image_mask, 
                              hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(mask_codes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, vl_mask, image_mask, code, n);
+  return hipGetLastError();
+}
+
+// Stream compaction of the admitted VL rows: one workgroup of 1024 threads; thread t owns a
+// contiguous chunk, chunk counts are scanned in LDS, then every thread writes its indices.
+__global__ __launch_bounds__(1024) void compact_rows_kernel(const uint8_t* code, int n, int* idx, int* count) {
+  __shared__ int cnt[1024];
+  const int t = threadIdx.x;
+  const int chunk = (n + 1023) / 1024;
+  const int lo = min(n, t * chunk), hi = min(n, lo + chunk);
+  int c = 0;
+  for (int r = lo; r < hi; ++r) c += code[r] != 0;
+  cnt[t] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = t >= off ? cnt[t - off] : 0;
+    __syncthreads();
+    cnt[t] += v;
+    __syncthreads();
+  }
+  int pos = cnt[t] - c;
+  for (int r = lo; r < hi; ++r)
+    if (code[r] != 0) idx[pos++] = r;
+  if (t == 1023) *count = cnt[1023];
+}
+
+hipError_t launch_compact_rows(const uint8_t* code, int n, int* idx, int* count, hipStream_t s) {
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, s, code, n, idx, count);
   return hipGetLastError();
 }
 

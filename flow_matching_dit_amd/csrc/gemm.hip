@@ -266,14 +266,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * MF_LDS_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * MF_LDS_LD];
 
+  if (a.rows_dev) {  // row count known on the device only: the grid covers the maximum,
+    // the tiles of the actual rows are dealt over all workgroup ids (and so all XCDs)
+    a.rows = min(a.rows, *a.rows_dev);
+    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
+  }
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
   int tm, tn;
   tile_of<GM>(nm, nn, tm, tn);
-  if (a.rows_dev) {  // row count known on the device only: tiles past it have no work
-    const int rr = min(a.rows, *a.rows_dev);
-    if (tm * BM >= rr) return;
-    a.rows = rr;
-  }
   const int g = blockIdx.y;
   const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
@@ -419,24 +419,83 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
 
   // acc[i][j][q]: row m = r0 + wm*TM + i*16 + lane%16, column n = n0 + wn*TN + j*16 + 4*(lane/16) + q
   const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
-    if (n >= a.N) continue;
-    float sc[4], bi[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
-      bi[q] = (a.bias && add_bias) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
-    }
+  if constexpr (EK == EPI_HEADS) {
+    // head-major scatter: the element offset splits into a row part (sample, position)
+    // and a column part (section, head, head dim); both are decomposed once per fragment
+    int rb[FM], rp[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = r0 + wm * TM + i * 16 + (lane & 15);
-      if (r < a.rows) {
+      const long row = r < a.rows ? (e.row_map ? (long)e.row_map[r] : (long)r) : 0;
+      rb[i] = (int)(row / e.pos_per_b);
+      rp[i] = (int)(row - (long)rb[i] * e.pos_per_b);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
+      if (n >= a.N) continue;
+      const int sec = n / e.width;
+      const int which = sec % e.nwhich;
+      const int layer = sec / e.nwhich;
+      const int c = n - sec * e.width;
+      const int head = c / e.hd;
+      const int d = c - head * e.hd;
+      const long ps = e.pstride[which];
+      const bool tr = e.transposed[which] != 0;
+      const long colpart = (long)layer * e.layer_stride[which] + (tr ? ((long)head * e.hd + d) * ps : (long)head * ps * e.hd + d);
+      const long bstride = (long)e.nh * ps * e.hd;  // elements per sample in either layout
+      float sc[4], bi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+        bi[q] = a.bias ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+      }
+      uint16_t* base16 = (uint16_t*)e.heads[which];
+      float* base32 = (float*)e.heads[which];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = r0 + wm * TM + i * 16 + (lane & 15);
+        if (r >= a.rows) continue;
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
-        epi_store<EK, 4>(e, g, r, n, v, cat, split);
+        for (int q = 0; q < 4; ++q) v[q] = apply_act(e.act, acc[i][j][q] * sc[q] + bi[q]);
+        const long idx = colpart + (long)rb[i] * bstride + (tr ? (long)rp[i] : (long)rp[i] * e.hd);
+        if (tr) {
+          if (e.out_f32) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) base32[idx + q * ps] = v[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) base16[idx + q * ps] = f_to_bf16(v[q]);
+          }
+        } else if (e.out_f32) {
+          *(float4*)(base32 + idx) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *(uint2*)(base16 + idx) = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
+                                               (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
+      if (n >= a.N) continue;
+      float sc[4], bi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+        bi[q] = (a.bias && add_bias) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = r0 + wm * TM + i * 16 + (lane & 15);
+        if (r < a.rows) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
+          epi_store<EK, 4>(e, g, r, n, v, cat, split);
+        }
       }
     }
   }

@@ -1,12 +1,15 @@
 // GEMMs of the action head for gfx950.
 //
-//  * gemm_mfma_kernel: bf16 activations x (bf16 | e4m3) weights on the matrix cores
+//  * gemm_dma_kernel: bf16 activations x bf16 weights on the matrix cores
 //    (v_mfma_f32_16x16x32_bf16), fp32 accumulation. Tiles of A [BM x 64] and
-//    W [BN x 64] go global -> registers -> LDS (double buffered; the next tile's
-//    buffer loads are in flight while the current tile's MFMAs run). Loads use
-//    buffer descriptors, so rows or k beyond the matrix read as zero without
-//    branches. e4m3 weights are decoded to bf16 (exactly) on their way into LDS and
-//    the per-column scale is applied in the epilogue.
+//    W [BN x 64] go from memory straight into LDS (buffer_load ... lds) through a
+//    ring of 3 stages, so two tiles of loads are in flight while one is multiplied.
+//  * gemm_mfma_kernel: the same product for e4m3 weights (and the small tiles).
+//    Tiles go global -> registers -> LDS (double buffered); e4m3 weights are decoded
+//    to bf16 (exactly) on their way into LDS and the per-column scale is applied in
+//    the epilogue.
+//    Both load through buffer descriptors, so rows or k beyond the matrix read as
+//    zero without branches.
 //    The MFMA computes C^T = W A^T per 16x16 fragment, so every lane ends with four
 //    consecutive output columns of one row: the epilogue stores 8 or 16 bytes per lane.
 //    Workgroups are numbered so that consecutive tiles share weight columns and land
@@ -21,6 +24,8 @@
 // per-sample weight gather of the per-embodiment linear (the batched product over
 // W[ids] on the architecture page, "Embodiment-specific projectors"), and finish
 // with a fused epilogue (bias, activation, residual add, head-major scatter, Euler).
+#include <type_traits>
+
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -246,6 +251,97 @@ __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
   tn = in / gm;
 }
 
+// Epilogue of the MFMA tile kernels: acc[i][j][q] holds row
+// r0 + wm*TM + i*16 + lane%16 and column n0 + wn*TN + j*16 + 4*(lane/16) + q.
+template <int BM, int BN, int WM, int WN, int EK>
+__device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
+                                              const floatx4_t (&acc)[BM / WM / 16][BN / WN / 16], int g, int cat,
+                                              int split, int r0, int n0, int wm, int wn, int lane) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
+  if constexpr (EK == EPI_HEADS) {
+    // head-major scatter: the element offset splits into a row part (sample, position)
+    // and a column part (section, head, head dim); both are decomposed once per fragment
+    int rb[FM], rp[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = r0 + wm * TM + i * 16 + (lane & 15);
+      const long row = r < a.rows ? (e.row_map ? (long)e.row_map[r] : (long)r) : 0;
+      rb[i] = (int)(row / e.pos_per_b);
+      rp[i] = (int)(row - (long)rb[i] * e.pos_per_b);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
+      if (n >= a.N) continue;
+      const int sec = n / e.width;
+      const int which = sec % e.nwhich;
+      const int layer = sec / e.nwhich;
+      const int c = n - sec * e.width;
+      const int head = c / e.hd;
+      const int d = c - head * e.hd;
+      const long ps = e.pstride[which];
+      const bool tr = e.transposed[which] != 0;
+      const long colpart = (long)layer * e.layer_stride[which] + (tr ? ((long)head * e.hd + d) * ps : (long)head * ps * e.hd + d);
+      const long bstride = (long)e.nh * ps * e.hd;  // elements per sample in either layout
+      float sc[4], bi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+        bi[q] = a.bias ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+      }
+      uint16_t* base16 = (uint16_t*)e.heads[which];
+      float* base32 = (float*)e.heads[which];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = r0 + wm * TM + i * 16 + (lane & 15);
+        if (r >= a.rows) continue;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = apply_act(e.act, acc[i][j][q] * sc[q] + bi[q]);
+        const long idx = colpart + (long)rb[i] * bstride + (tr ? (long)rp[i] : (long)rp[i] * e.hd);
+        if (tr) {
+          if (e.out_f32) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) base32[idx + q * ps] = v[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) base16[idx + q * ps] = f_to_bf16(v[q]);
+          }
+        } else if (e.out_f32) {
+          *(float4*)(base32 + idx) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *(uint2*)(base16 + idx) = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
+                                               (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
+      if (n >= a.N) continue;
+      float sc[4], bi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
+        bi[q] = (a.bias && add_bias) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = r0 + wm * TM + i * 16 + (lane & 15);
+        if (r < a.rows) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
+          epi_store<EK, 4>(e, g, r, n, v, cat, split);
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int BK, bool FP8, int EK, int PF = 1, int WPE = 1, int PAD = 8, int GM = 16>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE))) void gemm_mfma_kernel(GemmArgs a,
                                                                                                             Epi e) {
@@ -417,88 +513,183 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
     }
   }
 
-  // acc[i][j][q]: row m = r0 + wm*TM + i*16 + lane%16, column n = n0 + wn*TN + j*16 + 4*(lane/16) + q
-  const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
-  if constexpr (EK == EPI_HEADS) {
-    // head-major scatter: the element offset splits into a row part (sample, position)
-    // and a column part (section, head, head dim); both are decomposed once per fragment
-    int rb[FM], rp[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = r0 + wm * TM + i * 16 + (lane & 15);
-      const long row = r < a.rows ? (e.row_map ? (long)e.row_map[r] : (long)r) : 0;
-      rb[i] = (int)(row / e.pos_per_b);
-      rp[i] = (int)(row - (long)rb[i] * e.pos_per_b);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
-      if (n >= a.N) continue;
-      const int sec = n / e.width;
-      const int which = sec % e.nwhich;
-      const int layer = sec / e.nwhich;
-      const int c = n - sec * e.width;
-      const int head = c / e.hd;
-      const int d = c - head * e.hd;
-      const long ps = e.pstride[which];
-      const bool tr = e.transposed[which] != 0;
-      const long colpart = (long)layer * e.layer_stride[which] + (tr ? ((long)head * e.hd + d) * ps : (long)head * ps * e.hd + d);
-      const long bstride = (long)e.nh * ps * e.hd;  // elements per sample in either layout
-      float sc[4], bi[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
-        bi[q] = a.bias ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
-      }
-      uint16_t* base16 = (uint16_t*)e.heads[which];
-      float* base32 = (float*)e.heads[which];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = r0 + wm * TM + i * 16 + (lane & 15);
-        if (r >= a.rows) continue;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = apply_act(e.act, acc[i][j][q] * sc[q] + bi[q]);
-        const long idx = colpart + (long)rb[i] * bstride + (tr ? (long)rp[i] : (long)rp[i] * e.hd);
-        if (tr) {
-          if (e.out_f32) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) base32[idx + q * ps] = v[q];
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) base16[idx + q * ps] = f_to_bf16(v[q]);
-          }
-        } else if (e.out_f32) {
-          *(float4*)(base32 + idx) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          *(uint2*)(base16 + idx) = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                                               (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
-      if (n >= a.N) continue;
-      float sc[4], bi[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sc[q] = a.wscale ? a.wscale[(long)cat * a.s_cstride + n + q] : 1.0f;
-        bi[q] = (a.bias && add_bias) ? a.bias[(long)cat * a.b_cstride + n + q] : 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = r0 + wm * TM + i * 16 + (lane & 15);
-        if (r < a.rows) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
-          epi_store<EK, 4>(e, g, r, n, v, cat, split);
-        }
-      }
-    }
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
+}
+
+// ------------------------------------------------------------------------------------
+// bf16 x bf16 MFMA GEMM whose tiles go straight from memory into LDS
+// (buffer_load_dwordx4 ... lds, gfx950), through a ring of ST stages: the loads of
+// tile kt + ST - 1 are issued while tile kt is multiplied, so a load has ST - 1 tiles
+// of MFMAs to arrive, and no staging registers are needed. A wave's load instruction
+// writes 64 consecutive 16-byte LDS chunks (lane l -> chunk l), so the layout is chosen
+// through the global address each lane reads: row r of a tile keeps its k-chunk c at
+// chunk position c ^ ((r / SW) % CPR), with SW rows per 256 bytes of LDS. The 16 rows
+// one MFMA fragment read touches then fall on 16 distinct 16-byte bank groups.
+// The accumulation order (k-tiles in order, 32 k per MFMA) is that of gemm_mfma_kernel.
+// ------------------------------------------------------------------------------------
+// Waits until at most N vector-memory operations of this wave are in flight and all its
+// LDS reads have completed, then meets the workgroup barrier. One asm statement, so the
+// compiler moves no LDS access across it.
+// 16 bytes per lane from the buffer at byte offset off into LDS at lds + 16 * lane
+// (lds must be the same for the whole wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi e) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int CPR = BK / 8;       // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;     // tile rows per wave load instruction
+  constexpr int SW = 16 / CPR;      // tile rows per 256 bytes of LDS
+  constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);  // load instructions per wave and stage
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
+  static_assert(FM >= 1 && FN >= 1, "tile shape");
+  static_assert(ST >= 2 && ST <= 4, "2 to 4 stages");
+  constexpr int PER_STAGE = A_I + B_I;
+  static_assert(PER_STAGE * (ST - 1) < 64, "vmcnt range");
+
+  // One array per stage: the compiler's wait-count tracking then knows that loads into
+  // one stage do not alias reads of another (one shared ring would make every LDS read
+  // wait for all loads in flight).
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * BK], As1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t As2[ST > 2 ? BM * BK : 8], As3[ST > 3 ? BM * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BN * BK], Bs1[BN * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs2[ST > 2 ? BN * BK : 8], Bs3[ST > 3 ? BN * BK : 8];
+  auto stage_a = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return As0;
+    else if constexpr (decltype(st)::value == 1) return As1;
+    else if constexpr (decltype(st)::value == 2) return As2;
+    else return As3;
+  };
+  auto stage_b = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return Bs0;
+    else if constexpr (decltype(st)::value == 1) return Bs1;
+    else if constexpr (decltype(st)::value == 2) return Bs2;
+    else return Bs3;
+  };
+
+  if (a.rows_dev) {
+    a.rows = min(a.rows, *a.rows_dev);
+    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
   }
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of<GM>(nm, nn, tm, tn);
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
+  const int cat = a.ids ? a.ids[g] : 0;
+  const int r0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * a.k_per_split;
+  const int kend = min(a.K, kbeg + a.k_per_split);
+
+  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * 2));
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // This lane's chunk in load instruction i: tile row (wave * X_I + i) * RPI + lane / CPR,
+  // LDS position lane % CPR, holding k-chunk position ^ ((row / SW) % CPR).
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  int aoff[A_I], boff[B_I], akc[A_I], bkc[B_I];
+#pragma unroll
+  for (int i = 0; i < A_I; ++i) {
+    const int row = (wave * A_I + i) * RPI + lrow;
+    aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
+    akc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_I; ++i) {
+    const int row = (wave * B_I + i) * RPI + lrow;
+    boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
+    bkc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+  }
+  // Loads of k-tile kt into stage st. Every step issues its loads, also past the last
+  // k-tile (those read out of range: zeros, no memory traffic), so the number of loads
+  // in flight is the same at every step.
+  auto issue = [&](auto st, int kt) {
+    uint16_t* sa = stage_a(st);
+    uint16_t* sb = stage_b(st);
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_I; ++i)
+      dma16(ra_rsrc, sa + (wave * A_I + i) * 64 * 8,
+            (k0 + akc[i] < kend && aoff[i] != OOB) ? aoff[i] + (k0 + akc[i]) * 2 : OOB);
+#pragma unroll
+    for (int i = 0; i < B_I; ++i)
+      dma16(rw_rsrc, sb + (wave * B_I + i) * 64 * 8,
+            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + (k0 + bkc[i]) * 2 : OOB);
+  };
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Fragment reads: row (wm*TM + i*16 + lane%16) of A, k-chunk ks*4 + lane/16; the row's
+  // swizzle term depends on lane%16 only (fragment rows start at multiples of 16).
+  const int fsw = ((lane & 15) / SW) % CPR;
+  auto compute = [&](auto st) {
+    const uint16_t* sa = stage_a(st);
+    const uint16_t* sb = stage_b(st);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int pos = ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
+      bf16x8_t af[FM], wf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16 + (lane & 15)) * BK + pos];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16 + (lane & 15)) * BK + pos];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Step kt (stage kt % ST): wait for its loads (the ST - 2 later stages stay in flight)
+  // and for every wave to be done with the stage read in the previous step, refill that
+  // stage with k-tile kt + ST - 1, multiply.
+  auto step = [&](auto st, int kt) {
+    wait_vm_barrier<PER_STAGE * (ST - 2)>();
+    issue(ic<(decltype(st)::value + ST - 1) % ST>{}, kt + ST - 1);
+    compute(st);
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  issue(ic<0>{}, 0);
+  if constexpr (ST > 2) issue(ic<1>{}, 1);
+  if constexpr (ST > 3) issue(ic<2>{}, 2);
+  int kt = 0;
+  for (; kt + ST <= nk; kt += ST) {
+    step(ic<0>{}, kt);
+    step(ic<1>{}, kt + 1);
+    if constexpr (ST > 2) step(ic<2>{}, kt + 2);
+    if constexpr (ST > 3) step(ic<3>{}, kt + 3);
+  }
+  if (kt < nk) step(ic<0>{}, kt);
+  if constexpr (ST > 2) if (kt + 1 < nk) step(ic<1>{}, kt + 1);
+  if constexpr (ST > 3) if (kt + 2 < nk) step(ic<2>{}, kt + 2);
+  // no load may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -672,6 +863,25 @@ static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, int splits,
 //   2: 64x128, 4 waves, BK 64                    (fewer tiles: D-wide outputs, split-K)
 //   3: 32x64, 4 waves                            (<= 32 rows)
 //   4: 16x64, 4 waves                            (<= 16 rows)
+template <int BM, int BN, int WM, int WN, int BK, int ST, int GM>
+static hipError_t dma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  dim3 grid(nm * nn, a.groups, splits);
+  dim3 blk(64 * WM * WN);
+#define GR00T_DMA_CASE(K) \
+  case K: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, BK, ST, K, GM>), grid, blk, 0, s, a, e); break;
+  switch (e.kind) {
+    GR00T_DMA_CASE(EPI_STORE)
+    GR00T_DMA_CASE(EPI_RESID_ADD)
+    GR00T_DMA_CASE(EPI_HEADS)
+    GR00T_DMA_CASE(EPI_EULER)
+    GR00T_DMA_CASE(EPI_PARTIAL)
+    default: return hipErrorInvalidValue;
+  }
+#undef GR00T_DMA_CASE
+  return hipGetLastError();
+}
+
 static int tile_choice(int rows, int N, int groups) {
   auto tiles = [&](int bm, int bn) { return (long)((rows + bm - 1) / bm) * ((N + bn - 1) / bn) * groups; };
   if (rows <= 16) return 4;
@@ -694,6 +904,10 @@ int gemm_mfma_splits(int rows, int N, int K, int groups) {
     if (K / s > 2048 && K % (64 * 3) == 0 && K / 3 <= 2048) s = 3;
     return s;
   }
+  // 256 x 128 tiles if some split depth of at least 1024 fills the chip with them
+  const long t256 = (long)((rows + 255) / 256) * ((N + 127) / 128) * groups;
+  for (int s = 1; s <= 8 && K / s >= 1024; ++s)
+    if (K % (64 * s) == 0 && t256 * s >= 240) return s;
   int best = 1;
   for (int s = 1; s <= 8; ++s) {
     if (K % (64 * s) != 0) continue;
@@ -723,7 +937,12 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     if (a.rows <= 32) return skinny_go<2>(a, e, fp8, splits, s);
     return skinny_go<4>(a, e, fp8, splits, s);
   }
-  switch (tile_choice(a.rows, a.N, a.groups * splits)) {
+  const int cfg = tile_choice(a.rows, a.N, a.groups * splits);
+  if (!fp8) {  // bf16 weights: tiles straight into LDS through a 3-stage ring
+    if (cfg <= 1) return dma_kind<256, 128, 4, 2, 64, 3, 8>(a, e, splits, s);
+    if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16>(a, e, splits, s);
+  }
+  switch (cfg) {
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);
     case 1: return mfma_go<256, 128, 4, 2, 64, 16, 8>(a, e, fp8, splits, s);
     case 2: return mfma_go<64, 128, 2, 2, 64, 16, 16>(a, e, fp8, splits, s);

@@ -31,7 +31,6 @@
 
 namespace gr00t {
 
-typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float apply_act(int act, float v) {
   switch (act) {
@@ -206,16 +205,6 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
 // ------------------------------------------------------------------------------------
 // MFMA GEMM
 // ------------------------------------------------------------------------------------
-constexpr int OOB = 0x7FFFFFF0;  // buffer offset that is always out of range (reads 0)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  int32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
 
 // e4m3 code -> bf16 bits without branches.
 __device__ __forceinline__ uint32_t e4m3_bf16_nb(uint32_t c) {

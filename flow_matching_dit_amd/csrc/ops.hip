@@ -294,6 +294,81 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
 }
 
+// K fragments of the two 16-key halves of key tile kt (row r of half th is key
+// 8*(r/4) + 4*th + r%4, so lane group g ends with the scores of keys 8g .. 8g+7) and the
+// V^T fragments (head dim hf*16 + c16, keys 8g .. +7). Rows of the tile past Lk hold
+// finite values (the caller's padding contract) and get weight 0.
+template <int HD>
+__device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int Lp, int kt, int g,
+                                               int c16, bf16x8_v (&kf)[2][(HD + 31) / 32], bf16x8_v (&vf)[HD / 16]) {
+  constexpr int KS = (HD + 31) / 32, HF = HD / 16;
+  const int base = kt * 32;
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    const int key = base + 8 * (c16 >> 2) + 4 * th + (c16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 32 + g * 8;  // head dims past HD read 0 (zero padding of the last k step)
+      kf[th][ks] = __builtin_bit_cast(bf16x8_v, buf_load16(kr, d0 < HD ? (key * HD + d0) * 2 : OOB));
+    }
+  }
+#pragma unroll
+  for (int hf = 0; hf < HF; ++hf)
+    vf[hf] = __builtin_bit_cast(bf16x8_v, buf_load16(vr, ((hf * 16 + c16) * Lp + base + 8 * g) * 2));
+}
+
+// One key tile of the online softmax: scores S^T = K Q^T on the matrix cores, running
+// max m and sum l per query (exp2 with log2(e)/sqrt(hd) folded into sl2), O^T += V^T P^T.
+// mybits: admitted-key bits of keys 8g .. 8g+7 of the tile.
+template <int HD, int QF>
+__device__ __forceinline__ void attn_tile(const bf16x8_v (&qfr)[QF][(HD + 31) / 32], floatx4_t (&acc)[QF][HD / 16],
+                                          float (&m)[QF], float (&l)[QF], const bf16x8_v (&kf)[2][(HD + 31) / 32],
+                                          const bf16x8_v (&vf)[HD / 16], uint32_t mybits, float sl2) {
+  constexpr int KS = (HD + 31) / 32, HF = HD / 16;
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    floatx4_t sc[2];
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      floatx4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[th][ks], qfr[qf][ks], z, 0, 0, 0);
+      sc[th] = z;
+    }
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sv = sc[i >> 2][i & 3] * sl2;
+      x[i] = ((mybits >> i) & 1u) ? sv : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(m[qf], tmax);
+    const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m[qf] - mnew);
+    float psum = 0.0f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = (x[i] == -INFINITY) ? 0.0f : exp2f(x[i] - mnew);
+      const float p1 = (x[i + 1] == -INFINITY) ? 0.0f : exp2f(x[i + 1] - mnew);
+      psum += p0 + p1;
+      pk[i >> 1] = (uint32_t)f_to_bf16(p0) | ((uint32_t)f_to_bf16(p1) << 16);
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l[qf] = l[qf] * alpha + psum;
+    m[qf] = mnew;
+    const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf) {
+      acc[qf][hf] *= alpha;
+      acc[qf][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hf], pf, acc[qf][hf], 0, 0, 0);
+    }
+  }
+}
+
 template <int HD, int QF, int NW>
 __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   constexpr int KS = (HD + 31) / 32;  // 32-wide k steps over the head dim (zero padded)
@@ -308,8 +383,8 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   const int S = a.S, Lk = a.Lk, Lp = a.Lp, nh = a.nh;
   const long bh = (long)b * nh + h;
   const uint16_t* q = (const uint16_t*)a.q + bh * S * HD;
-  const uint16_t* k = (const uint16_t*)a.k + bh * Lp * HD;
-  const uint16_t* vt = (const uint16_t*)a.vt + bh * HD * Lp;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + bh * Lp * HD, (uint32_t)(Lp * HD * 2));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.vt + bh * HD * Lp, (uint32_t)(Lp * HD * 2));
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
 
   // Q^T fragments: lane holds query qf*16 + c16, head dims 32*ks + 8g .. +7
@@ -342,68 +417,6 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
     const unsigned long long bal = __ballot(admit);
     return (uint32_t)(bal >> (8 * g)) & 0xFFu;
   };
-  // K fragments of the two 16-key halves (row r of half th is key 8*(r/4) + 4*th + r%4)
-  // and V^T fragments (head dim hf*16 + c16, keys 8g .. +7) of tile kt
-  auto load_tile = [&](int kt, bf16x8_v (&kf)[2][KS], bf16x8_v (&vf)[HF]) {
-    const int base = kt * 32;
-#pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      const int key = base + 8 * (c16 >> 2) + 4 * th + (c16 & 3);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = ks * 32 + g * 8;
-        kf[th][ks] = __builtin_bit_cast(bf16x8_v, ld16_or_zero(k + (long)key * HD + d0, d0 < HD));
-      }
-    }
-#pragma unroll
-    for (int hf = 0; hf < HF; ++hf)
-      vf[hf] = __builtin_bit_cast(bf16x8_v, *(const uint4*)(vt + (long)(hf * 16 + c16) * Lp + base + 8 * g));
-  };
-  auto process = [&](const bf16x8_v (&kf)[2][KS], const bf16x8_v (&vf)[HF], uint32_t mybits) {
-#pragma unroll
-    for (int qf = 0; qf < QF; ++qf) {
-      floatx4_t sc[2];
-#pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        floatx4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[th][ks], qfr[qf][ks], z, 0, 0, 0);
-        sc[th] = z;
-      }
-      float x[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float sv = sc[i >> 2][i & 3] * sl2;
-        x[i] = ((mybits >> i) & 1u) ? sv : -INFINITY;
-        tmax = fmaxf(tmax, x[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(m[qf], tmax);
-      const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m[qf] - mnew);
-      float psum = 0.0f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float p0 = (x[i] == -INFINITY) ? 0.0f : exp2f(x[i] - mnew);
-        const float p1 = (x[i + 1] == -INFINITY) ? 0.0f : exp2f(x[i + 1] - mnew);
-        psum += p0 + p1;
-        pk[i >> 1] = (uint32_t)f_to_bf16(p0) | ((uint32_t)f_to_bf16(p1) << 16);
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l[qf] = l[qf] * alpha + psum;
-      m[qf] = mnew;
-      const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#pragma unroll
-      for (int hf = 0; hf < HF; ++hf) {
-        acc[qf][hf] *= alpha;
-        acc[qf][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hf], pf, acc[qf][hf], 0, 0, 0);
-      }
-    }
-  };
-
   // wave w takes tiles w, w + NW, ...; two tiles' loads are issued before either is used
   const int ntiles = (Lk + 31) / 32;
   for (int kt = wave; kt < ntiles; kt += 2 * NW) {
@@ -412,10 +425,10 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
     const uint32_t bits1 = kt2 < ntiles ? tile_bits(kt2) : 0u;
     const bool any0 = __ballot(bits0 != 0) != 0ull, any1 = __ballot(bits1 != 0) != 0ull;
     bf16x8_v kf0[2][KS], vf0[HF], kf1[2][KS], vf1[HF];
-    if (any0) load_tile(kt, kf0, vf0);
-    if (any1) load_tile(kt2, kf1, vf1);
-    if (any0) process(kf0, vf0, bits0);
-    if (any1) process(kf1, vf1, bits1);
+    if (any0) attn_load_tile<HD>(kr, vr, Lp, kt, g, c16, kf0, vf0);
+    if (any1) attn_load_tile<HD>(kr, vr, Lp, kt2, g, c16, kf1, vf1);
+    if (any0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, sl2);
+    if (any1) attn_tile<HD, QF>(qfr, acc, m, l, kf1, vf1, bits1, sl2);
   }
 
   // merge the waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16
@@ -450,6 +463,118 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   }
 }
 
+// One wave per (sample, head) pair, four pairs per workgroup: the wave streams every key
+// tile of its pair through the online softmax with the next tile's loads in flight, and
+// writes its own output (no merge across waves). The admitted-key bitmap of the pair is
+// built first (one ballot per 64 keys, loads of 8 words issued together) so that tiles
+// without an admitted key are skipped without loading them.
+constexpr int AW_MAXWORDS = 8;  // keys per pair <= 512 (one mask byte per lane and word)
+constexpr int AW_SETS = 2;  // register sets of the key-tile ring (deeper rings cost occupancy)
+template <int HD, int QF, int NS, bool MASK>
+__global__ __launch_bounds__(256) void attention_wave_kernel(AttnArgs a) {
+  constexpr int KS = (HD + 31) / 32, HF = HD / 16;
+  __shared__ unsigned long long words_s[4][AW_MAXWORDS];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: descriptors in SGPRs
+  const int g = lane >> 4, c16 = lane & 15;
+  const int pair = blockIdx.x * 4 + wave;
+  if (pair >= a.B * a.nh) return;  // whole wave; the kernel has no workgroup barrier
+  const int S = a.S, Lk = a.Lk, Lp = a.Lp, nh = a.nh;
+  const int b = pair / nh, h = pair - b * nh;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + (long)pair * S * HD, (uint32_t)(S * HD * 2));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + (long)pair * Lp * HD, (uint32_t)(Lp * HD * 2));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.vt + (long)pair * HD * Lp, (uint32_t)(Lp * HD * 2));
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+  const int ntiles = (Lk + 31) / 32;
+
+  // Every load below is a buffer load issued by every lane (out-of-range lanes read 0)
+  // and independent of data loaded before it, so the loads of one phase are in flight
+  // together and the compiler's wait counts stay exact.
+  // Mask bytes first (the ballots wait for them alone); keys >= Lk read 0.
+  uint8_t mb[AW_MAXWORDS];
+  if constexpr (MASK) {
+    const __amdgpu_buffer_rsrc_t mr = make_rsrc(a.mask + (long)b * Lk, (uint32_t)Lk);
+#pragma unroll
+    for (int u = 0; u < AW_MAXWORDS; ++u) mb[u] = buf_load1(mr, u * 64 + lane);
+  }
+  // Q^T fragments: lane holds query qf*16 + c16, head dims 32*ks + 8g .. +7
+  bf16x8_v qfr[QF][KS];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int qi = qf * 16 + c16, d0 = ks * 32 + g * 8;
+      qfr[qf][ks] = __builtin_bit_cast(bf16x8_v, buf_load16(qr, (qi < S && d0 < HD) ? (qi * HD + d0) * 2 : OOB));
+    }
+  // the first NS key tiles, before their masks are known (every tile below ntiles lies
+  // inside the padded key rows)
+  bf16x8_v kf[NS][2][KS], vf[NS][HF];
+#pragma unroll
+  for (int sidx = 0; sidx < NS; ++sidx) attn_load_tile<HD>(kr, vr, Lp, min(sidx, ntiles - 1), g, c16, kf[sidx], vf[sidx]);
+
+  // admitted-key bitmap: word w holds keys 64w .. 64w+63 (Lk <= 64 * AW_MAXWORDS)
+#pragma unroll
+  for (int u = 0; u < AW_MAXWORDS; ++u) {
+    const int j = u * 64 + lane;
+    bool adm;
+    if constexpr (MASK) adm = (mb[u] & a.mask_bit) != 0;
+    else adm = j < Lk;
+    const unsigned long long bal = __ballot(adm);
+    if (lane == 0) words_s[wave][u] = bal;
+  }
+  // 32-bit admitted mask of key tile kt (0 <= kt < ntiles)
+  auto tile_mask = [&](int kt) -> uint32_t { return (uint32_t)(words_s[wave][kt >> 1] >> (32 * (kt & 1))); };
+  // first and last tile with an admitted key (t1 < 0: none)
+  int t0 = ntiles, t1 = -1;
+  for (int c0 = 0; c0 < ntiles; c0 += 64) {
+    const int kt = c0 + lane;
+    const unsigned long long bal = __ballot(kt < ntiles && tile_mask(kt < ntiles ? kt : 0) != 0u);
+    if (bal) {
+      t0 = min(t0, c0 + (int)__builtin_ctzll(bal));
+      t1 = c0 + 63 - (int)__builtin_clzll(bal);
+    }
+  }
+
+  floatx4_t acc[QF][HF];
+  float m[QF], l[QF];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    m[qf] = -INFINITY;
+    l[qf] = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf) acc[qf][hf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // ring of NS register sets over tiles 0 .. t1: set kt % NS holds tile kt when tile kt
+  // is processed; after use it is refilled with tile kt + NS, clamped into [t0, t1] (a
+  // clamped refill below t0 is replaced before use; one above t1 is never used)
+  for (int kt0 = 0; kt0 <= t1; kt0 += NS) {
+#pragma unroll
+    for (int sidx = 0; sidx < NS; ++sidx) {
+      const int kt = kt0 + sidx;
+      const uint32_t mt = kt <= t1 ? tile_mask(kt) : 0u;
+      if (mt) attn_tile<HD, QF>(qfr, acc, m, l, kf[sidx], vf[sidx], (mt >> (8 * g)) & 0xFFu, sl2);
+      attn_load_tile<HD>(kr, vr, Lp, min(max(kt + NS, t0), t1), g, c16, kf[sidx], vf[sidx]);
+    }
+  }
+
+  // O^T: lane holds head dims hf*16 + 4g + i of query qf*16 + c16
+  uint16_t* o = (uint16_t*)a.o;
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    const int qi = qf * 16 + c16;
+    if (qi >= S) continue;
+    const float inv = l[qf] > 0.0f ? 1.0f / l[qf] : 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < HF; ++hf) {
+      const floatx4_t v = acc[qf][hf] * inv;
+      *(uint2*)(o + ((long)(b * S + qi) * nh + h) * HD + hf * 16 + 4 * g) =
+          make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
+                     (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+    }
+  }
+}
+
 // 8 waves for small batches with few query fragments (B = 1 latency: more key tiles in
 // flight per head); 4 waves otherwise (enough workgroups fill the chip; smaller merge).
 template <int HD>
@@ -457,6 +582,17 @@ static hipError_t attn_mfma_hd(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.nh, a.B);
   const int qf = (a.S + 15) / 16;
   const bool wide = a.B * a.nh < 512;
+  if (a.B * a.nh >= 1024 && a.Lk <= 64 * AW_MAXWORDS && qf <= 2) {
+    const dim3 wgrid((a.B * a.nh + 3) / 4);
+    if (a.mask) {
+      if (qf == 1) hipLaunchKernelGGL((attention_wave_kernel<HD, 1, AW_SETS, true>), wgrid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attention_wave_kernel<HD, 2, AW_SETS, true>), wgrid, dim3(256), 0, s, a);
+    } else {
+      if (qf == 1) hipLaunchKernelGGL((attention_wave_kernel<HD, 1, AW_SETS, false>), wgrid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attention_wave_kernel<HD, 2, AW_SETS, false>), wgrid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   switch (qf) {
     case 1:
       if (wide) hipLaunchKernelGGL((attention_mfma_kernel<HD, 1, 8>), grid, dim3(512), 0, s, a);

@@ -56,6 +56,12 @@ def test_small_width_parity(name, kw):
     _parity(small(name, **kw))
 
 
+def test_wave_per_head_attention_parity():
+    # 64 samples x 16 heads of width 48: at >= 1024 (sample, head) pairs attention runs one
+    # wave per pair (ragged VL lengths, skipped key tiles); the oracle runs on sampled rows
+    _parity(small("dit32_bf16_b64", batch=64, num_heads=16, hidden=768, ff_dim=1536), samples=[0, 29, 63])
+
+
 def test_small_width_graph_parity_ragged():
     _parity(small("dit32_bf16_b64", batch=8), flags=H.FLAG_USE_GRAPH | H.FLAG_STRICT, prepare=True)
 

@@ -24,6 +24,7 @@
 // per-sample weight gather of the per-embodiment linear (the batched product over
 // W[ids] on the architecture page, "Embodiment-specific projectors"), and finish
 // with a fused epilogue (bias, activation, residual add, head-major scatter, Euler).
+#include <algorithm>
 #include <type_traits>
 
 #include "kcommon.h"
@@ -681,6 +682,156 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
 }
 
+// Variant with the MFMA fragments double buffered in registers: while the MFMAs of
+// k-tile kt run from one register set, the fragments of k-tile kt + 1 are read from LDS
+// into the other, so the matrix cores do not wait for LDS within a step. LDS stage
+// kt % ST is refilled with k-tile kt + ST as soon as every wave has read it (one step
+// later), so ST - 1 tiles of loads are in flight while one is multiplied.
+template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma2_kernel(GemmArgs a, Epi e) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int KSN = BK / 32;       // MFMA k steps per tile
+  constexpr int CPR = BK / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int SW = 16 / CPR;
+  constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
+  static_assert(ST == 3, "three stages (the step body is unrolled over 6 = lcm(3, 2) steps)");
+  constexpr int PER_STAGE = A_I + B_I;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * BK], As1[BM * BK], As2[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BN * BK], Bs1[BN * BK], Bs2[BN * BK];
+  auto stage_a = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return As0;
+    else if constexpr (decltype(st)::value == 1) return As1;
+    else return As2;
+  };
+  auto stage_b = [&](auto st) -> uint16_t* {
+    if constexpr (decltype(st)::value == 0) return Bs0;
+    else if constexpr (decltype(st)::value == 1) return Bs1;
+    else return Bs2;
+  };
+
+  if (a.rows_dev) {
+    a.rows = min(a.rows, *a.rows_dev);
+    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
+  }
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of<GM>(nm, nn, tm, tn);
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
+  const int cat = a.ids ? a.ids[g] : 0;
+  const int r0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * a.k_per_split;
+  const int kend = min(a.K, kbeg + a.k_per_split);
+
+  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * 2));
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  int aoff[A_I], boff[B_I], akc[A_I], bkc[B_I];
+#pragma unroll
+  for (int i = 0; i < A_I; ++i) {
+    const int row = (wave * A_I + i) * RPI + lrow;
+    aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
+    akc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_I; ++i) {
+    const int row = (wave * B_I + i) * RPI + lrow;
+    boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
+    bkc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+  }
+  auto issue = [&](auto st, int kt) {
+    uint16_t* sa = stage_a(st);
+    uint16_t* sb = stage_b(st);
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_I; ++i)
+      dma16(ra_rsrc, sa + (wave * A_I + i) * 64 * 8,
+            (k0 + akc[i] < kend && aoff[i] != OOB) ? aoff[i] + (k0 + akc[i]) * 2 : OOB);
+#pragma unroll
+    for (int i = 0; i < B_I; ++i)
+      dma16(rw_rsrc, sb + (wave * B_I + i) * 64 * 8,
+            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + (k0 + bkc[i]) * 2 : OOB);
+  };
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  bf16x8_t fa[2][KSN][FM], fw[2][KSN][FN];
+  const int fsw = ((lane & 15) / SW) % CPR;
+  auto lds_read = [&](auto st, auto set) {
+    constexpr int R = decltype(set)::value;
+    const uint16_t* sa = stage_a(st);
+    const uint16_t* sb = stage_b(st);
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks) {
+      const int pos = ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[R][ks][i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16 + (lane & 15)) * BK + pos];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fw[R][ks][j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16 + (lane & 15)) * BK + pos];
+    }
+  };
+  auto mfmas = [&](auto set) {
+    constexpr int R = decltype(set)::value;
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[R][ks][j], fa[R][ks][i], acc[i][j], 0, 0, 0);
+  };
+  // Step kt (U = kt % 6): stage kt + 1 landed (stage kt + 2 may still be in flight) and
+  // every wave is done with its reads of stage kt % 3 (made in step kt - 1); refill that
+  // stage with k-tile kt + 3, read the fragments of k-tile kt + 1, multiply k-tile kt.
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  auto step = [&](auto u, int kt) {
+    constexpr int U = decltype(u)::value;
+    wait_vm_barrier<PER_STAGE>();
+    issue(ic<U % 3>{}, kt + 3);
+    if (kt + 1 < nk) lds_read(ic<(U + 1) % 3>{}, ic<(U + 1) % 2>{});
+    mfmas(ic<U % 2>{});
+  };
+
+  issue(ic<0>{}, 0);
+  issue(ic<1>{}, 1);
+  issue(ic<2>{}, 2);
+  wait_vm_barrier<2 * PER_STAGE>();
+  lds_read(ic<0>{}, ic<0>{});
+  int kt = 0;
+  for (; kt + 6 <= nk; kt += 6) {
+    step(ic<0>{}, kt);
+    step(ic<1>{}, kt + 1);
+    step(ic<2>{}, kt + 2);
+    step(ic<3>{}, kt + 3);
+    step(ic<4>{}, kt + 4);
+    step(ic<5>{}, kt + 5);
+  }
+  if (kt < nk) step(ic<0>{}, kt);
+  if (kt + 1 < nk) step(ic<1>{}, kt + 1);
+  if (kt + 2 < nk) step(ic<2>{}, kt + 2);
+  if (kt + 3 < nk) step(ic<3>{}, kt + 3);
+  if (kt + 4 < nk) step(ic<4>{}, kt + 4);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
+}
+
 // ------------------------------------------------------------------------------------
 // Skinny MFMA GEMM for <= 64 rows per group (weight streaming: B = 1 projections and
 // the per-embodiment linears). A workgroup owns 16 output columns; its NWAVE waves take
@@ -771,6 +922,139 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
   }
 }
 
+// Variant for bf16 weights whose activation rows of the split fit in LDS: every workgroup
+// reads the same few rows, and fetching them per lane as 16-row fragments costs more
+// than the weight stream itself. Instead the workgroup copies its rows into LDS once
+// (coalesced loads straight into LDS, rows padded by 16 bytes so that the 16 rows of a
+// fragment read fall on distinct bank groups), while each wave's weight loads for its
+// whole slice of K (at most KC k-steps) are already in flight.
+constexpr int SKL_MAX_LDS = 64 * 1024;
+template <int MF, int NC, int NWAVE, int EK>
+__global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a, Epi e) {
+  constexpr int KC = 8;
+  extern __shared__ __attribute__((aligned(1024))) uint16_t skl[];
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
+  const int cat = a.ids ? a.ids[g] : 0;
+  const int n0 = blockIdx.x * 16 * NC;  // NC 16-column fragments per workgroup
+  const int t = threadIdx.x, lane = t & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * 2));
+  const int kbeg = split * a.k_per_split, kend = min(a.K, kbeg + a.k_per_split);
+  const int kper = a.k_per_split;            // multiple of 128
+  const int rs = kper + 8;                   // padded LDS row (elements)
+  const int cpr = rs / 8;                    // 16-byte chunks per padded row
+  const int tc = a.rows * cpr;               // chunks of the staged rows
+
+  // 0. the bias of the outputs this thread writes in 4. (first, so its latency overlaps the rest)
+  float4 bias4[(NC * MF * 64 + 64 * NWAVE - 1) / (64 * NWAVE)];
+#pragma unroll
+  for (int u = 0; u < (NC * MF * 64 + 64 * NWAVE - 1) / (64 * NWAVE); ++u) {
+    const int p = t + u * 64 * NWAVE, f = p >> 6, n = n0 + (f / MF) * 16 + 4 * ((p & 63) >> 4);
+    bias4[u] = (a.bias && (EK != EPI_PARTIAL || split == 0) && p < NC * MF * 64 && n < a.N)
+                   ? *(const float4*)(a.bias + (long)cat * a.b_cstride + n)
+                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  // 1. activation rows [0, rows) x [kbeg, kbeg + kper) -> LDS (chunk c: row c / cpr, k-chunk c % cpr;
+  //    the padding chunk and k past kend read 0)
+  for (int j = wave; j * 64 < tc; j += NWAVE) {
+    const int c = j * 64 + lane;
+    const int row = c / cpr, kc = c - row * cpr;
+    const int k = kbeg + kc * 8;
+    const bool in = c < tc && kc < cpr - 1 && k < kend;
+    dma16(ra_rsrc, skl + j * 64 * 8, in ? (row * (int)a.lda + k) * 2 : OOB);
+  }
+  // the weight loads below must be issued after these (the wait in 3. counts on it)
+  asm volatile("" ::: "memory");
+  // 2. this wave's weight fragments: k-steps [s0, s1) of 32 of the split, NC column fragments
+  const int nsteps = (kend - kbeg + 31) / 32;
+  const int spw = (nsteps + NWAVE - 1) / NWAVE;
+  const int s0 = wave * spw, s1 = min(nsteps, s0 + spw);
+  int woff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) woff[c] = (n0 + c * 16 + lr < a.N) ? (n0 + c * 16 + lr) * a.K * 2 : OOB;
+  uint4 wv[KC][NC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int k = kbeg + (s0 + i) * 32 + lg * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      wv[i][c] = buf_load16(rw_rsrc, (s0 + i < s1 && k < kend && woff[c] != OOB) ? woff[c] + k * 2 : OOB);
+  }
+  // 3. the staged rows are complete (weight loads may still be in flight)
+  wait_vm_barrier<KC * NC>();
+  floatx4_t acc[NC][MF];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) acc[c][mf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    if (s0 + i < s1) {
+      const int kk = (s0 + i) * 32 + lg * 8;
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        const int row = mf * 16 + lr;
+        const uint4 av = *(const uint4*)&skl[min(row, a.rows - 1) * rs + kk];
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, row < a.rows ? av : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[c][mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[i][c]), af, acc[c][mf], 0, 0, 0);
+      }
+    }
+  }
+  // 4. the waves' partial sums, added in wave order through LDS (reusing the staged rows)
+  __syncthreads();
+  floatx4_t* red = (floatx4_t*)skl;  // [NWAVE][NC * MF][64]
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) red[(wave * NC * MF + c * MF + mf) * 64 + lane] = acc[c][mf];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < (NC * MF * 64 + 64 * NWAVE - 1) / (64 * NWAVE); ++u) {
+    const int p = t + u * 64 * NWAVE;
+    if (p >= NC * MF * 64) break;
+    const int f = p >> 6, ln = p & 63;  // f = c * MF + mf
+    floatx4_t sum = red[f * 64 + ln];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) sum += red[(w * NC * MF + f) * 64 + ln];
+    const int r = (f % MF) * 16 + (ln & 15);
+    const int n = n0 + (f / MF) * 16 + 4 * (ln >> 4);
+    if (r < a.rows && n < a.N) {
+      float v[4] = {sum[0] + bias4[u].x, sum[1] + bias4[u].y, sum[2] + bias4[u].z, sum[3] + bias4[u].w};
+      epi_store<EK, 4>(e, g, r, n, v, cat, split);
+    }
+  }
+}
+
+// LDS bytes gemm_skinny_lds_kernel needs (0 = does not fit).
+static size_t skinny_lds_bytes(const GemmArgs& a, int mf, int nc, int nwave) {
+  const long tc = (long)a.rows * ((a.k_per_split + 8) / 8);
+  const long bytes = std::max(((tc + 63) / 64) * 64 * 16, (long)nwave * nc * mf * 1024);
+  return bytes <= SKL_MAX_LDS ? (size_t)bytes : 0;
+}
+
+template <int MF, int NC, int NWAVE>
+static hipError_t skinny_lds_kind(const GemmArgs& a, const Epi& e, int splits, size_t lds, hipStream_t s) {
+  dim3 grid((a.N + 16 * NC - 1) / (16 * NC), a.groups, splits), blk(64 * NWAVE);
+#define GR00T_SKL_CASE(K) \
+  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K>), grid, blk, lds, s, a, e); break;
+  switch (e.kind) {
+    GR00T_SKL_CASE(EPI_STORE)
+    GR00T_SKL_CASE(EPI_RESID_ADD)
+    GR00T_SKL_CASE(EPI_HEADS)
+    GR00T_SKL_CASE(EPI_EULER)
+    GR00T_SKL_CASE(EPI_PARTIAL)
+    default: return hipErrorInvalidValue;
+  }
+#undef GR00T_SKL_CASE
+  return hipGetLastError();
+}
+
 template <int MF, int NWAVE, bool FP8>
 static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
   dim3 grid((a.N + 15) / 16, a.groups, splits), blk(64 * NWAVE);
@@ -790,6 +1074,12 @@ static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, int splits, hipSt
 
 template <int MF>
 static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
+  // one chunk of KC = 8 k-steps per wave: 8 waves cover a split of up to 2048, 4 up to 1024
+  const int nwave = a.k_per_split >= 1024 ? 8 : 4;
+  if (!fp8 && a.k_per_split <= nwave * 256 && (a.k_per_split % 128) == 0) {
+    const size_t lds = skinny_lds_bytes(a, MF, 1, nwave);
+    if (lds) return nwave == 8 ? skinny_lds_kind<MF, 1, 8>(a, e, splits, lds, s) : skinny_lds_kind<MF, 1, 4>(a, e, splits, lds, s);
+  }
   if (a.k_per_split >= 1024)
     return fp8 ? skinny_kind<MF, 8, true>(a, e, splits, s) : skinny_kind<MF, 8, false>(a, e, splits, s);
   return fp8 ? skinny_kind<MF, 4, true>(a, e, splits, s) : skinny_kind<MF, 4, false>(a, e, splits, s);
@@ -891,6 +1181,8 @@ int gemm_mfma_splits(int rows, int N, int K, int groups) {
     int s = 1;
     while (K / s > 2048 && s < 8 && K % (64 * s * 2) == 0) s *= 2;
     if (K / s > 2048 && K % (64 * 3) == 0 && K / 3 <= 2048) s = 3;
+    // few column blocks (narrow N): split deeper until >= 256 workgroups, keeping K / s >= 384
+    while ((long)((N + 15) / 16) * groups * s < 256 && s < 8 && K % (128 * s * 2) == 0 && K / (s * 2) >= 384) s *= 2;
     return s;
   }
   // 256 x 128 tiles if some split depth of at least 1024 fills the chip with them

@@ -67,7 +67,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// erf from Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
+// (|error| <= 1.5e-7): one reciprocal, one exponential and a degree-5 polynomial, with no
+// branches, for the GELU in GEMM epilogues.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return copysignf(1.0f - poly * __expf(-ax * ax), x);
+}
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
 // Buffer-descriptor loads: an offset past the descriptor's byte range reads 0 (no fault,

@@ -204,7 +204,7 @@ def main():
     ap.add_argument("--b1-workload", default="dit32_bf16_b1")
     ap.add_argument("--b1-steps", type=int, default=30)
     ap.add_argument("--profile-calls", type=int, default=2)
-    ap.add_argument("--cpu-samples", type=int, default=3)
+    ap.add_argument("--cpu-samples", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for HBM byte counters)")

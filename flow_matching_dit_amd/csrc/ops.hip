@@ -279,20 +279,20 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Attention on the matrix cores (bf16): one workgroup (4 waves) per (head, sample);
-// wave w takes the 32-key tiles w, w+4, ... For a tile, S^T = K Q^T is formed per
+// Attention on the matrix cores (bf16). For a 32-key tile, S^T = K Q^T is formed per
 // 16-query fragment with v_mfma_f32_16x16x32_bf16, so each lane holds the scores of
 // one query against 8 keys; the tile's keys are enumerated so that those 8 keys are
 // contiguous, which makes the exponentiated scores directly the B operand of
 // O^T += V^T P^T (values cached transposed, [hd][L]). Running max / sum in fp32 with
-// exp2; tiles with no admitted key are skipped; the 4 waves' partial results are
-// merged through LDS at the end.
+// exp2; tiles with no admitted key are not multiplied.
+//  * attention_mfma_kernel: one workgroup (4 or 8 waves) per (head, sample); wave w
+//    takes the tiles w, w+NW, ...; the waves' partial results are merged through LDS.
+//    For few (sample, head) pairs (small batches).
+//  * attention_wave_kernel: one wave per (sample, head) streaming all its tiles; for
+//    many pairs.
 // ------------------------------------------------------------------------------------
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
-  return ok ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
-}
 
 // K fragments of the two 16-key halves of key tile kt (row r of half th is key
 // 8*(r/4) + 4*th + r%4, so lane group g ends with the scores of keys 8g .. 8g+7) and the
@@ -382,9 +382,10 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int S = a.S, Lk = a.Lk, Lp = a.Lp, nh = a.nh;
   const long bh = (long)b * nh + h;
-  const uint16_t* q = (const uint16_t*)a.q + bh * S * HD;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + bh * S * HD, (uint32_t)(S * HD * 2));
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + bh * Lp * HD, (uint32_t)(Lp * HD * 2));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.vt + bh * HD * Lp, (uint32_t)(Lp * HD * 2));
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(a.mask ? a.mask + (long)b * Lk : nullptr, a.mask ? (uint32_t)Lk : 0u);
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
 
   // Q^T fragments: lane holds query qf*16 + c16, head dims 32*ks + 8g .. +7
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int qi = qf * 16 + c16, d0 = ks * 32 + g * 8;
-      qfr[qf][ks] = __builtin_bit_cast(bf16x8_v, ld16_or_zero(q + (long)qi * HD + d0, qi < S && d0 < HD));
+      qfr[qf][ks] = __builtin_bit_cast(bf16x8_v, buf_load16(qr, (qi < S && d0 < HD) ? (qi * HD + d0) * 2 : OOB));
     }
 
   floatx4_t acc[QF][HF];
@@ -407,28 +408,26 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
     for (int hf = 0; hf < HF; ++hf) acc[qf][hf] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // admitted-key bits of tile kt for this lane (keys 8g .. 8g+7 of the tile); 0 past the end
-  auto tile_bits = [&](int kt) -> uint32_t {
-    bool admit = false;
-    if (lane < 32) {
-      const int j = kt * 32 + lane;
-      admit = j < Lk && (a.mask == nullptr || (a.mask[(long)b * Lk + j] & a.mask_bit));
-    }
-    const unsigned long long bal = __ballot(admit);
-    return (uint32_t)(bal >> (8 * g)) & 0xFFu;
-  };
-  // wave w takes tiles w, w + NW, ...; two tiles' loads are issued before either is used
+  // wave w takes tiles w, w + NW, ... two at a time. Both tiles' K/V loads are issued
+  // before their mask bytes are read (tiles below ntiles lie inside the padded key rows;
+  // a second tile past the end reloads the last one and is not used), so the mask and the
+  // tiles cost one memory latency, not two.
   const int ntiles = (Lk + 31) / 32;
   for (int kt = wave; kt < ntiles; kt += 2 * NW) {
     const int kt2 = kt + NW;
-    const uint32_t bits0 = tile_bits(kt);
-    const uint32_t bits1 = kt2 < ntiles ? tile_bits(kt2) : 0u;
-    const bool any0 = __ballot(bits0 != 0) != 0ull, any1 = __ballot(bits1 != 0) != 0ull;
     bf16x8_v kf0[2][KS], vf0[HF], kf1[2][KS], vf1[HF];
-    if (any0) attn_load_tile<HD>(kr, vr, Lp, kt, g, c16, kf0, vf0);
-    if (any1) attn_load_tile<HD>(kr, vr, Lp, kt2, g, c16, kf1, vf1);
-    if (any0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, sl2);
-    if (any1) attn_tile<HD, QF>(qfr, acc, m, l, kf1, vf1, bits1, sl2);
+    attn_load_tile<HD>(kr, vr, Lp, kt, g, c16, kf0, vf0);
+    attn_load_tile<HD>(kr, vr, Lp, min(kt2, ntiles - 1), g, c16, kf1, vf1);
+    asm volatile("" ::: "memory");
+    // admitted-key bits of the two tiles (lanes < 32: key kt*32 + lane); keys past Lk read 0
+    const uint8_t mb0 = buf_load1(mr, kt * 32 + (lane & 31));
+    const uint8_t mb1 = buf_load1(mr, kt2 * 32 + (lane & 31));
+    const bool ad0 = lane < 32 && kt * 32 + lane < Lk && (a.mask == nullptr || (mb0 & a.mask_bit) != 0);
+    const bool ad1 = lane < 32 && kt2 < ntiles && kt2 * 32 + lane < Lk && (a.mask == nullptr || (mb1 & a.mask_bit) != 0);
+    const unsigned long long bal0 = __ballot(ad0), bal1 = __ballot(ad1);
+    const uint32_t bits0 = (uint32_t)(bal0 >> (8 * g)) & 0xFFu, bits1 = (uint32_t)(bal1 >> (8 * g)) & 0xFFu;
+    if (bal0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, sl2);
+    if (bal1) attn_tile<HD, QF>(qfr, acc, m, l, kf1, vf1, bits1, sl2);
   }
 
   // merge the waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16

@@ -243,10 +243,13 @@ __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
 
 // Epilogue of the MFMA tile kernels: acc[i][j][q] holds row
 // r0 + wm*TM + i*16 + lane%16 and column n0 + wn*TN + j*16 + 4*(lane/16) + q.
+// res (EPI_RESID_ADD only, may be null): the residual values of acc's positions, loaded by
+// the caller ahead of time; the epilogue then stores res + v without reading the output.
 template <int BM, int BN, int WM, int WN, int EK>
 __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
                                               const floatx4_t (&acc)[BM / WM / 16][BN / WN / 16], int g, int cat,
-                                              int split, int r0, int n0, int wm, int wn, int lane) {
+                                              int split, int r0, int n0, int wm, int wn, int lane,
+                                              const float4* res = nullptr) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
@@ -325,7 +328,13 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * sc[q] + bi[q];
-          epi_store<EK, 4>(e, g, r, n, v, cat, split);
+          if (EK == EPI_RESID_ADD && res != nullptr && e.add_tab == nullptr && e.act == ACT_NONE) {
+            const float4 o = res[i * FN + j];
+            *(float4*)((float*)e.out + ((long)g * e.out_gstride + e.out_row_off + r) * e.out_ld + n) =
+                make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+          } else {
+            epi_store<EK, 4>(e, g, r, n, v, cat, split);
+          }
         }
       }
     }
@@ -632,6 +641,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // residual add: this lane's residual values are loaded now (the oldest loads in flight),
+  // so the epilogue does not wait for them
+  float4 res[EK == EPI_RESID_ADD ? FM * FN : 1];
+  if constexpr (EK == EPI_RESID_ADD) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = r0 + wm * TM + i * 16 + (lane & 15);
+        const int n = n0 + wn * TN + j * 16 + (lane >> 4) * 4;
+        res[i * FN + j] = (r < a.rows && n < a.N)
+                              ? *(const float4*)((const float*)e.out + ((long)g * e.out_gstride + e.out_row_off + r) * e.out_ld + n)
+                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    asm volatile("" ::: "memory");
+  }
 
   // Fragment reads: row (wm*TM + i*16 + lane%16) of A, k-chunk ks*4 + lane/16; the row's
   // swizzle term depends on lane%16 only (fragment rows start at multiples of 16).
@@ -679,7 +704,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   if constexpr (ST > 3) if (kt + 2 < nk) step(ic<2>{}, kt + 2);
   // no load may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane,
+                                    EK == EPI_RESID_ADD ? res : nullptr);
 }
 
 // Variant with the MFMA fragments double buffered in registers: while the MFMAs of
@@ -1168,13 +1194,14 @@ static int tile_choice(int rows, int N, int groups) {
   if (rows <= 64) return 2;
   if (tiles(256, 128) >= 512) return 0;
   if (tiles(256, 128) >= 160) return 1;
+  if (N <= 2048) return 5;  // narrow outputs: 64 x 64 tiles
   return 2;
 }
 
 // Smallest split count that gives >= 240 workgroups (or leaves <= 512 k per split),
 // else the largest valid one (at most 8, each split a multiple of 64 deep).
 int gemm_mfma_splits(int rows, int N, int K, int groups) {
-  static const int bm[5] = {256, 256, 64, 32, 16}, bn[5] = {128, 128, 128, 64, 64};
+  static const int bm[6] = {256, 256, 64, 32, 16, 64}, bn[6] = {128, 128, 128, 64, 64, 64};
   if (rows <= 64) {
     // skinny kernel: 8 waves split K inside a workgroup, each holding one chunk of 8 k-steps
     // (256 deep) in flight; deeper K is split across workgroups
@@ -1222,8 +1249,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
   if (!fp8) {  // bf16 weights: tiles straight into LDS through a 3-stage ring
     if (cfg <= 1) return dma_kind<256, 128, 4, 2, 64, 3, 8>(a, e, splits, s);
     if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16>(a, e, splits, s);
+    if (cfg == 5) return dma_kind<64, 64, 2, 2, 64, 3, 16>(a, e, splits, s);
   }
-  switch (cfg) {
+  switch (cfg == 5 ? 2 : cfg) {  // e4m3 weights: 64 x 128 tiles for narrow outputs too
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);
     case 1: return mfma_go<256, 128, 4, 2, 64, 16, 8>(a, e, fp8, splits, s);
     case 2: return mfma_go<64, 128, 2, 2, 64, 16, 16>(a, e, fp8, splits, s);

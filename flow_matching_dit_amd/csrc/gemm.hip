@@ -544,6 +544,16 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N - 1>{}) in order (compile-time indices).
+template <typename F, int... I>
+__device__ __forceinline__ void for_seq_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void for_seq(F&& f) {
+  for_seq_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi e) {
   constexpr int NW = WM * WN;
@@ -556,7 +566,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
   static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
   static_assert(FM >= 1 && FN >= 1, "tile shape");
-  static_assert(ST >= 2 && ST <= 4, "2 to 4 stages");
+  static_assert(ST >= 2 && ST <= 6, "2 to 6 stages");
   constexpr int PER_STAGE = A_I + B_I;
   static_assert(PER_STAGE * (ST - 1) < 64, "vmcnt range");
 
@@ -565,19 +575,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   // wait for all loads in flight).
   __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * BK], As1[BM * BK];
   __shared__ __attribute__((aligned(1024))) uint16_t As2[ST > 2 ? BM * BK : 8], As3[ST > 3 ? BM * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t As4[ST > 4 ? BM * BK : 8], As5[ST > 5 ? BM * BK : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BN * BK], Bs1[BN * BK];
   __shared__ __attribute__((aligned(1024))) uint16_t Bs2[ST > 2 ? BN * BK : 8], Bs3[ST > 3 ? BN * BK : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs4[ST > 4 ? BN * BK : 8], Bs5[ST > 5 ? BN * BK : 8];
   auto stage_a = [&](auto st) -> uint16_t* {
-    if constexpr (decltype(st)::value == 0) return As0;
-    else if constexpr (decltype(st)::value == 1) return As1;
-    else if constexpr (decltype(st)::value == 2) return As2;
-    else return As3;
+    constexpr int V = decltype(st)::value;
+    if constexpr (V == 0) return As0;
+    else if constexpr (V == 1) return As1;
+    else if constexpr (V == 2) return As2;
+    else if constexpr (V == 3) return As3;
+    else if constexpr (V == 4) return As4;
+    else return As5;
   };
   auto stage_b = [&](auto st) -> uint16_t* {
-    if constexpr (decltype(st)::value == 0) return Bs0;
-    else if constexpr (decltype(st)::value == 1) return Bs1;
-    else if constexpr (decltype(st)::value == 2) return Bs2;
-    else return Bs3;
+    constexpr int V = decltype(st)::value;
+    if constexpr (V == 0) return Bs0;
+    else if constexpr (V == 1) return Bs1;
+    else if constexpr (V == 2) return Bs2;
+    else if constexpr (V == 3) return Bs3;
+    else if constexpr (V == 4) return Bs4;
+    else return Bs5;
   };
 
   if (a.rows_dev) {
@@ -642,9 +660,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // residual add: this lane's residual values are loaded now (the oldest loads in flight),
-  // so the epilogue does not wait for them
-  float4 res[EK == EPI_RESID_ADD ? FM * FN : 1];
-  if constexpr (EK == EPI_RESID_ADD) {
+  // so the epilogue does not wait for them (wave tiles of up to 8 fragments: more would spill)
+  constexpr bool PRE = EK == EPI_RESID_ADD && FM * FN <= 8;
+  float4 res[PRE ? FM * FN : 1];
+  if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -689,23 +708,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   };
 
   const int nk = (kend - kbeg + BK - 1) / BK;
-  issue(ic<0>{}, 0);
-  if constexpr (ST > 2) issue(ic<1>{}, 1);
-  if constexpr (ST > 3) issue(ic<2>{}, 2);
+  for_seq<ST - 1>([&](auto i) { issue(i, decltype(i)::value); });
   int kt = 0;
-  for (; kt + ST <= nk; kt += ST) {
-    step(ic<0>{}, kt);
-    step(ic<1>{}, kt + 1);
-    if constexpr (ST > 2) step(ic<2>{}, kt + 2);
-    if constexpr (ST > 3) step(ic<3>{}, kt + 3);
-  }
-  if (kt < nk) step(ic<0>{}, kt);
-  if constexpr (ST > 2) if (kt + 1 < nk) step(ic<1>{}, kt + 1);
-  if constexpr (ST > 3) if (kt + 2 < nk) step(ic<2>{}, kt + 2);
+  for (; kt + ST <= nk; kt += ST) for_seq<ST>([&](auto i) { step(i, kt + decltype(i)::value); });
+  for_seq<ST - 1>([&](auto i) {
+    if (kt + decltype(i)::value < nk) step(i, kt + decltype(i)::value);
+  });
   // no load may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane,
-                                    EK == EPI_RESID_ADD ? res : nullptr);
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane, PRE ? res : nullptr);
 }
 
 // Variant with the MFMA fragments double buffered in registers: while the MFMAs of
@@ -1247,7 +1258,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
   }
   const int cfg = tile_choice(a.rows, a.N, a.groups * splits);
   if (!fp8) {  // bf16 weights: tiles straight into LDS through a 3-stage ring
-    if (cfg <= 1) return dma_kind<256, 128, 4, 2, 64, 3, 8>(a, e, splits, s);
+    // 16 waves (4 per SIMD): measured 4-8% faster than 8 waves with 64 x 64 wave tiles
+    if (cfg == 0) return dma_kind<256, 256, 4, 4, 32, 4, 8>(a, e, splits, s);
+    if (cfg == 1) return dma_kind<256, 128, 4, 4, 64, 3, 8>(a, e, splits, s);
     if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16>(a, e, splits, s);
     if (cfg == 5) return dma_kind<64, 64, 2, 2, 64, 3, 16>(a, e, splits, s);
   }

@@ -166,3 +166,35 @@ def test_library_noise_is_standard_normal():
     say(f"[noise] mean {x.mean():.4f} std {x.std():.4f} n={x.size}")
     assert abs(x.mean()) < 0.03 and abs(x.std() - 1) < 0.03
     assert not np.array_equal(a, b)
+
+
+def test_horizon_permutation_equivariance(wl):
+    # the head has no positional term: permuting the action rows of the noise (and of the
+    # action mask) permutes action_pred the same way; self attention sums its keys in
+    # another order, so equality holds to fp32 rounding
+    w, wt, inp, nz = wl
+    h = build_head(w, wt)
+    y = gpu_action(h, inp, nz)
+    perm = np.random.default_rng(5).permutation(w.cfg.action_horizon)
+    inp2 = dict(inp)
+    if inp["action_mask"] is not None:
+        inp2["action_mask"] = np.ascontiguousarray(inp["action_mask"][:, perm])
+    yp = gpu_action(h, inp2, np.ascontiguousarray(nz[:, perm]))
+    h.close()
+    assert np.max(np.abs(yp - y[:, perm])) <= 1e-4 * np.max(np.abs(y))
+
+
+def test_unused_category_weights_do_not_matter(wl):
+    w, wt, inp, nz = wl
+    h = build_head(w, wt)
+    y = gpu_action(h, inp, nz)
+    h.close()
+    unused = sorted(set(range(w.cfg.num_categories)) - set(int(i) for i in inp["embodiment_id"]))
+    assert unused
+    wt2 = {k: v.copy() for k, v in wt.items()}
+    for name in ("state_enc.w1", "action_enc.w2", "action_dec.w1", "action_dec.b2"):
+        wt2[name][unused] = 7.0
+    h = build_head(w, wt2)
+    y2 = gpu_action(h, inp, nz)
+    h.close()
+    assert np.array_equal(y, y2)

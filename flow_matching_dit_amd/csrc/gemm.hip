@@ -1205,14 +1205,14 @@ static int tile_choice(int rows, int N, int groups) {
   if (rows <= 64) return 2;
   if (tiles(256, 128) >= 512) return 0;
   if (tiles(256, 128) >= 160) return 1;
-  if (N <= 2048) return 5;  // narrow outputs: 64 x 64 tiles
+  if (N <= 2048) return 5;  // narrow outputs: 128 x 64 tiles, 8 waves
   return 2;
 }
 
 // Smallest split count that gives >= 240 workgroups (or leaves <= 512 k per split),
 // else the largest valid one (at most 8, each split a multiple of 64 deep).
 int gemm_mfma_splits(int rows, int N, int K, int groups) {
-  static const int bm[6] = {256, 256, 64, 32, 16, 64}, bn[6] = {128, 128, 128, 64, 64, 64};
+  static const int bm[6] = {256, 256, 64, 32, 16, 128}, bn[6] = {128, 128, 128, 64, 64, 64};
   if (rows <= 64) {
     // skinny kernel: 8 waves split K inside a workgroup, each holding one chunk of 8 k-steps
     // (256 deep) in flight; deeper K is split across workgroups
@@ -1233,7 +1233,9 @@ int gemm_mfma_splits(int rows, int N, int K, int groups) {
     best = s;
     const int c = tile_choice(rows, N, groups * s);
     const long t = (long)((rows + bm[c] - 1) / bm[c]) * ((N + bn[c] - 1) / bn[c]) * groups * s;
-    if (t >= 240 || K / s <= 512) return s;
+    // narrow 128 x 64 tiles: 216 tiles at 1088 rows fill the chip well enough that splitting
+    // (and the partials the next norm must add) costs more than it gains
+    if (t >= (c == 5 ? 200 : 240) || K / s <= 512) return s;
   }
   return best;
 }
@@ -1262,7 +1264,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     if (cfg == 0) return dma_kind<256, 256, 4, 4, 32, 4, 8>(a, e, splits, s);
     if (cfg == 1) return dma_kind<256, 128, 4, 4, 64, 3, 8>(a, e, splits, s);
     if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16>(a, e, splits, s);
-    if (cfg == 5) return dma_kind<64, 64, 2, 2, 64, 3, 16>(a, e, splits, s);
+    if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 3, 16>(a, e, splits, s);
   }
   switch (cfg == 5 ? 2 : cfg) {  // e4m3 weights: 64 x 128 tiles for narrow outputs too
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);

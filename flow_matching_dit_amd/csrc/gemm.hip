@@ -67,8 +67,8 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
     } else {
       uint16_t* p = (uint16_t*)e.out + idx;
       if (NV == 4) {
-        *(uint2*)p = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                                (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+        *(uint2*)p = make_uint2(bf16x2_bits(v[0], v[1]),
+                                bf16x2_bits(v[2], v[3]));
       } else {
 #pragma unroll
         for (int q = 0; q < NV; ++q) p[q] = f_to_bf16(v[q]);
@@ -127,8 +127,8 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
       } else {
         uint16_t* p = (uint16_t*)e.heads[which] + idx;
         if (NV == 4) {
-          *(uint2*)p = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                                  (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+          *(uint2*)p = make_uint2(bf16x2_bits(v[0], v[1]),
+                                  bf16x2_bits(v[2], v[3]));
         } else {
 #pragma unroll
           for (int q = 0; q < NV; ++q) p[q] = f_to_bf16(v[q]);
@@ -305,8 +305,8 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
         } else if (e.out_f32) {
           *(float4*)(base32 + idx) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
-          *(uint2*)(base16 + idx) = make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                                               (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+          *(uint2*)(base16 + idx) = make_uint2(bf16x2_bits(v[0], v[1]),
+                                               bf16x2_bits(v[2], v[3]));
         }
       }
     }

@@ -21,10 +21,13 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN payloads are not preserved).
-__device__ __forceinline__ uint16_t f_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+typedef __bf16 bf16x2_n __attribute__((ext_vector_type(2)));
+typedef float floatx2_n __attribute__((ext_vector_type(2)));
+// two values -> packed bf16 pair (a in the low half), one instruction
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_n){a, b}, bf16x2_n));
 }
 
 // e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value).

@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict_
       if (sizeof(TY) == 4) {
         *(float4*)((float*)yr + c) = make_float4(o[0], o[1], o[2], o[3]);
       } else {
-        *(uint2*)((uint16_t*)yr + c) = make_uint2((uint32_t)f_to_bf16(o[0]) | ((uint32_t)f_to_bf16(o[1]) << 16),
-                                                  (uint32_t)f_to_bf16(o[2]) | ((uint32_t)f_to_bf16(o[3]) << 16));
+        *(uint2*)((uint16_t*)yr + c) = make_uint2(bf16x2_bits(o[0], o[1]),
+                                                  bf16x2_bits(o[2], o[3]));
       }
     }
   }
@@ -318,12 +318,14 @@ __device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t kr, __amdg
 }
 
 // One key tile of the online softmax: scores S^T = K Q^T on the matrix cores, running
-// max m and sum l per query (exp2 with log2(e)/sqrt(hd) folded into sl2), O^T += V^T P^T.
-// mybits: admitted-key bits of keys 8g .. 8g+7 of the tile.
+// max m (in units of log2 e / sqrt(hd), folded into sl2) and sum l per query, O^T += V^T P^T.
+// mybits: admitted-key bits of keys 8g .. 8g+7 of the tile; full: every key of the tile is
+// admitted (wave-uniform), so no key needs masking. The max is taken on the raw scores
+// (sl2 > 0) and each probability is exp2(score * sl2 - m) with one fma.
 template <int HD, int QF>
 __device__ __forceinline__ void attn_tile(const bf16x8_v (&qfr)[QF][(HD + 31) / 32], floatx4_t (&acc)[QF][HD / 16],
                                           float (&m)[QF], float (&l)[QF], const bf16x8_v (&kf)[2][(HD + 31) / 32],
-                                          const bf16x8_v (&vf)[HD / 16], uint32_t mybits, float sl2) {
+                                          const bf16x8_v (&vf)[HD / 16], uint32_t mybits, bool full, float sl2) {
   constexpr int KS = (HD + 31) / 32, HF = HD / 16;
 #pragma unroll
   for (int qf = 0; qf < QF; ++qf) {
@@ -335,32 +337,34 @@ __device__ __forceinline__ void attn_tile(const bf16x8_v (&qfr)[QF][(HD + 31) / 
       for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[th][ks], qfr[qf][ks], z, 0, 0, 0);
       sc[th] = z;
     }
-    float x[8];
     float tmax = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float sv = sc[i >> 2][i & 3] * sl2;
-      x[i] = ((mybits >> i) & 1u) ? sv : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
+      for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, sc[i >> 2][i & 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, ((mybits >> i) & 1u) ? sc[i >> 2][i & 3] : -INFINITY);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m[qf], tmax);
-    const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m[qf] - mnew);
-    float psum = 0.0f;
-    uint32_t pk[4];
+    const float mnew = fmaxf(m[qf], tmax * sl2);
+    const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qf] - mnew);
+    float p[8];
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float p0 = (x[i] == -INFINITY) ? 0.0f : exp2f(x[i] - mnew);
-      const float p1 = (x[i + 1] == -INFINITY) ? 0.0f : exp2f(x[i + 1] - mnew);
-      psum += p0 + p1;
-      pk[i >> 1] = (uint32_t)f_to_bf16(p0) | ((uint32_t)f_to_bf16(p1) << 16);
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mnew));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        p[i] = ((mybits >> i) & 1u) ? __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mnew)) : 0.0f;
     }
+    float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l[qf] = l[qf] * alpha + psum;
     m[qf] = mnew;
-    const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const bf16x8_v pf = __builtin_bit_cast(
+        bf16x8_v, make_uint4(bf16x2_bits(p[0], p[1]), bf16x2_bits(p[2], p[3]), bf16x2_bits(p[4], p[5]), bf16x2_bits(p[6], p[7])));
 #pragma unroll
     for (int hf = 0; hf < HF; ++hf) {
       acc[qf][hf] *= alpha;
@@ -426,8 +430,8 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
     const bool ad1 = lane < 32 && kt2 < ntiles && kt2 * 32 + lane < Lk && (a.mask == nullptr || (mb1 & a.mask_bit) != 0);
     const unsigned long long bal0 = __ballot(ad0), bal1 = __ballot(ad1);
     const uint32_t bits0 = (uint32_t)(bal0 >> (8 * g)) & 0xFFu, bits1 = (uint32_t)(bal1 >> (8 * g)) & 0xFFu;
-    if (bal0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, sl2);
-    if (bal1) attn_tile<HD, QF>(qfr, acc, m, l, kf1, vf1, bits1, sl2);
+    if (bal0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, (uint32_t)bal0 == 0xFFFFFFFFu, sl2);
+    if (bal1) attn_tile<HD, QF>(qfr, acc, m, l, kf1, vf1, bits1, (uint32_t)bal1 == 0xFFFFFFFFu, sl2);
   }
 
   // merge the waves: O^T rows (head dims hf*16 + 4g + i) of query qf*16 + c16
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(256) void attention_wave_kernel(AttnArgs a) {
     for (int sidx = 0; sidx < NS; ++sidx) {
       const int kt = kt0 + sidx;
       const uint32_t mt = kt <= t1 ? tile_mask(kt) : 0u;
-      if (mt) attn_tile<HD, QF>(qfr, acc, m, l, kf[sidx], vf[sidx], (mt >> (8 * g)) & 0xFFu, sl2);
+      if (mt) attn_tile<HD, QF>(qfr, acc, m, l, kf[sidx], vf[sidx], (mt >> (8 * g)) & 0xFFu, mt == 0xFFFFFFFFu, sl2);
       attn_load_tile<HD>(kr, vr, Lp, min(max(kt + NS, t0), t1), g, c16, kf[sidx], vf[sidx]);
     }
   }
@@ -568,8 +572,8 @@ __global__ __launch_bounds__(256) void attention_wave_kernel(AttnArgs a) {
     for (int hf = 0; hf < HF; ++hf) {
       const floatx4_t v = acc[qf][hf] * inv;
       *(uint2*)(o + ((long)(b * S + qi) * nh + h) * HD + hf * 16 + 4 * g) =
-          make_uint2((uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16),
-                     (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16));
+          make_uint2(bf16x2_bits(v[0], v[1]),
+                     bf16x2_bits(v[2], v[3]));
     }
   }
 }

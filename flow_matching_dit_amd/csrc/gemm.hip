@@ -241,6 +241,28 @@ __device__ __forceinline__ void tile_of(int nm, int nn, int& tm, int& tn) {
   tn = in / gm;
 }
 
+// Split-K launches (grid nb x 1 x S, S dividing 8, nb * S a multiple of 8): workgroups are
+// dealt round-robin over the 8 XCDs in dispatch order (x fastest, then z), so XCD
+// id % 8 is given the K-slice split = xcd / (8 / S) and a contiguous run of that slice's
+// tiles. Each XCD then reads only its slice of A (with the plain mapping every XCD reads
+// all of A once per slice). Bijective: split s takes positions [0, nb) from its 8 / S XCDs.
+template <int GM>
+__device__ __forceinline__ void split_tile_of(int nm, int nn, int S, int& tm, int& tn, int& split) {
+  const int nb = nm * nn;
+  const int id = (int)blockIdx.x + nb * (int)blockIdx.z;
+  const int xcd = id & 7, slot = id >> 3;
+  const int nslots = (nb * S) >> 3;
+  const int xps = 8 / S;
+  split = xcd / xps;
+  const int lid = (xcd % xps) * nslots + slot;
+  const int group = lid / (GM * nn);
+  const int first = group * GM;
+  const int gm = min(GM, nm - first);
+  const int in = lid - group * GM * nn;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
 // Epilogue of the MFMA tile kernels: acc[i][j][q] holds row
 // r0 + wm*TM + i*16 + lane%16 and column n0 + wn*TN + j*16 + 4*(lane/16) + q.
 // res (EPI_RESID_ADD only, may be null): the residual values of acc's positions, loaded by
@@ -603,10 +625,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
     if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
   }
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of<GM>(nm, nn, tm, tn);
+  int tm, tn, split;
+  if (gridDim.z > 1 && gridDim.y == 1 && (8 % gridDim.z) == 0 && ((nm * nn * (int)gridDim.z) & 7) == 0) {
+    split_tile_of<GM>(nm, nn, (int)gridDim.z, tm, tn, split);
+  } else {
+    tile_of<GM>(nm, nn, tm, tn);
+    split = blockIdx.z;
+  }
   const int g = blockIdx.y;
-  const int split = blockIdx.z;
   const int cat = a.ids ? a.ids[g] : 0;
   const int r0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * a.k_per_split;

@@ -109,14 +109,14 @@ __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, flo
     const long bh = (long)b * e.nh + head;
     const long ps = e.pstride[which];
     const long base = (long)layer * e.layer_stride[which];
-    if (e.transposed[which]) {
-      const long idx = base + (bh * e.hd + d) * ps + pos;
+    if (e.transposed[which]) {  // [pos / 32][hd][pos % 32] per (sample, head)
+      const long idx = base + bh * e.hd * ps + (long)(pos >> 5) * e.hd * 32 + d * 32 + (pos & 31);
       if (e.out_f32) {
 #pragma unroll
-        for (int q = 0; q < NV; ++q) ((float*)e.heads[which])[idx + q * ps] = v[q];
+        for (int q = 0; q < NV; ++q) ((float*)e.heads[which])[idx + q * 32] = v[q];
       } else {
 #pragma unroll
-        for (int q = 0; q < NV; ++q) ((uint16_t*)e.heads[which])[idx + q * ps] = f_to_bf16(v[q]);
+        for (int q = 0; q < NV; ++q) ((uint16_t*)e.heads[which])[idx + q * 32] = f_to_bf16(v[q]);
       }
     } else {
       const long idx = base + (bh * ps + pos) * e.hd + d;
@@ -298,7 +298,8 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
       const int d = c - head * e.hd;
       const long ps = e.pstride[which];
       const bool tr = e.transposed[which] != 0;
-      const long colpart = (long)layer * e.layer_stride[which] + (tr ? ((long)head * e.hd + d) * ps : (long)head * ps * e.hd + d);
+      // transposed: [pos / 32][hd][pos % 32] per (sample, head); else [pos][hd]
+      const long colpart = (long)layer * e.layer_stride[which] + (long)head * ps * e.hd + (tr ? d * 32 : d);
       const long bstride = (long)e.nh * ps * e.hd;  // elements per sample in either layout
       float sc[4], bi[4];
 #pragma unroll
@@ -315,14 +316,14 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = apply_act(e.act, acc[i][j][q] * sc[q] + bi[q]);
-        const long idx = colpart + (long)rb[i] * bstride + (tr ? (long)rp[i] : (long)rp[i] * e.hd);
+        const long idx = colpart + (long)rb[i] * bstride + (tr ? (long)(rp[i] >> 5) * e.hd * 32 + (rp[i] & 31) : (long)rp[i] * e.hd);
         if (tr) {
           if (e.out_f32) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) base32[idx + q * ps] = v[q];
+            for (int q = 0; q < 4; ++q) base32[idx + q * 32] = v[q];
           } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) base16[idx + q * ps] = f_to_bf16(v[q]);
+            for (int q = 0; q < 4; ++q) base16[idx + q * 32] = f_to_bf16(v[q]);
           }
         } else if (e.out_f32) {
           *(float4*)(base32 + idx) = make_float4(v[0], v[1], v[2], v[3]);

@@ -609,7 +609,7 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
     const int Lp = round32(L);
     e.pstride[0] = e.pstride[1] = Lp;
     e.transposed[0] = 0;
-    e.transposed[1] = 1;  // values cached [hd][L] for the attention's V^T operand
+    e.transposed[1] = 1;  // values cached [L/32][hd][32] for the attention's V^T operand
     e.layer_stride[0] = e.layer_stride[1] = (long)B * Lp * D;
     e.row_map = h->w.vrow;
     LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));

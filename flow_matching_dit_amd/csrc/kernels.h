@@ -53,7 +53,9 @@ struct Epi {
   // layer = sec / nwhich, head = (n % width) / hd, d = n % hd; row r -> (b, pos) with
   // pos_per_b positions per sample; element goes to heads[which] + layer * layer_stride[which] +
   //   ((b * nh + head) * pstride[which] + pos) * hd + d        (row-major positions), or
-  //   ((b * nh + head) * hd + d) * pstride[which] + pos        (transposed[which]: [hd][pos]).
+  //   (b * nh + head) * pstride[which] * hd + (pos / 32) * hd * 32 + d * 32 + pos % 32
+  //                                                 (transposed[which]: [pos / 32][hd][pos % 32];
+  //                                                  pstride a multiple of 32).
   void* heads[3];
   int nwhich;
   int width;
@@ -93,7 +95,7 @@ hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, l
 
 // Multi-head attention per (sample, head): softmax(q k^T / sqrt(hd)) v.
 // q [B][nh][S][hd]; k [B][nh][Lp][hd] (keys row-major, Lp = Lk rounded up to 32);
-// vt [B][nh][hd][Lp] (values transposed); o [B*S][nh*hd]; all in act dtype. Key rows
+// vt [B][nh][Lp/32][hd][32] (values transposed per 32-key tile); o [B*S][nh*hd]; all in act dtype. Key rows
 // and value columns in [Lk, Lp) must hold finite values (they get weight 0).
 // mask: NULL = every key admitted; else key j of sample b is admitted iff
 // (mask[b * Lk + j] & mask_bit) != 0. A query with no admitted key outputs 0.

@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
     }
     for (int i = t; i < AT_KC * hd; i += 256) {
       const int d = i / AT_KC, jj = i - d * AT_KC;
-      Vs[jj][d] = (jj < nk) ? ld(vt + (long)d * Lp + j0 + jj) : 0.0f;
+      const int pos = j0 + jj;  // values cached [pos / 32][hd][pos % 32]
+      Vs[jj][d] = (jj < nk) ? ld(vt + (long)(pos >> 5) * hd * 32 + d * 32 + (pos & 31)) : 0.0f;
     }
     if (t < AT_KC) adm[t] = (t < nk) && (a.mask == nullptr || (a.mask[(long)b * Lk + j0 + t] & a.mask_bit));
     __syncthreads();
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void attention_valu_kernel(AttnArgs a) {
 // 16-query fragment with v_mfma_f32_16x16x32_bf16, so each lane holds the scores of
 // one query against 8 keys; the tile's keys are enumerated so that those 8 keys are
 // contiguous, which makes the exponentiated scores directly the B operand of
-// O^T += V^T P^T (values cached transposed, [hd][L]). Running max / sum in fp32 with
+// O^T += V^T P^T (values cached transposed per 32-key tile, [L/32][hd][32]). Running max / sum in fp32 with
 // exp2; tiles with no admitted key are not multiplied.
 //  * attention_mfma_kernel: one workgroup (4 or 8 waves) per (head, sample); wave w
 //    takes the tiles w, w+NW, ...; the waves' partial results are merged through LDS.
@@ -296,7 +297,7 @@ typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 
 // K fragments of the two 16-key halves of key tile kt (row r of half th is key
 // 8*(r/4) + 4*th + r%4, so lane group g ends with the scores of keys 8g .. 8g+7) and the
-// V^T fragments (head dim hf*16 + c16, keys 8g .. +7). Rows of the tile past Lk hold
+// V^T fragments (head dim hf*16 + c16, keys 8g .. +7 of the tile). Rows of the tile past Lk hold
 // finite values (the caller's padding contract) and get weight 0.
 template <int HD>
 __device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int Lp, int kt, int g,
@@ -312,9 +313,10 @@ __device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t kr, __amdg
       kf[th][ks] = __builtin_bit_cast(bf16x8_v, buf_load16(kr, d0 < HD ? (key * HD + d0) * 2 : OOB));
     }
   }
+  // values cached [tile][hd][32]: the 16 head-dim rows of a fragment are 1 KB of contiguous memory
 #pragma unroll
   for (int hf = 0; hf < HF; ++hf)
-    vf[hf] = __builtin_bit_cast(bf16x8_v, buf_load16(vr, ((hf * 16 + c16) * Lp + base + 8 * g) * 2));
+    vf[hf] = __builtin_bit_cast(bf16x8_v, buf_load16(vr, ((kt * HD + hf * 16 + c16) * 32 + 8 * g) * 2));
 }
 
 // One key tile of the online softmax: scores S^T = K Q^T on the matrix cores, running

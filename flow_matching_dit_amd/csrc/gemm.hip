@@ -544,9 +544,13 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
 // tile kt + ST - 1 are issued while tile kt is multiplied, so a load has ST - 1 tiles
 // of MFMAs to arrive, and no staging registers are needed. A wave's load instruction
 // writes 64 consecutive 16-byte LDS chunks (lane l -> chunk l), so the layout is chosen
-// through the global address each lane reads: row r of a tile keeps its k-chunk c at
-// chunk position c ^ ((r / SW) % CPR), with SW rows per 256 bytes of LDS. The 16 rows
-// one MFMA fragment read touches then fall on 16 distinct 16-byte bank groups.
+// through the global address each lane reads.
+//  * BK = 64 (128-byte rows): row r keeps its k-chunk c at chunk position c ^ ((r / 2) % 8).
+//  * BK = 32 (64-byte rows): each block of 16 rows (1 KB, exactly what one MFMA fragment
+//    read covers) is held as 8 lines of 128 bytes; line L holds rows L and L + 8, and the
+//    chunk h = (row / 8) + 2 * c of either row sits at position h ^ L of the line.
+// Both keep every fragment read free of LDS bank conflicts (the plain row-major XOR for
+// 64-byte rows measured half of all LDS cycles as conflicts).
 // The accumulation order (k-tiles in order, 32 k per MFMA) is that of gemm_mfma_kernel.
 // ------------------------------------------------------------------------------------
 // Waits until at most N vector-memory operations of this wave are in flight and all its
@@ -648,21 +652,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   const int wave = t >> 6, lane = t & 63;
   const int wm = wave / WN, wn = wave % WN;
 
-  // This lane's chunk in load instruction i: tile row (wave * X_I + i) * RPI + lane / CPR,
-  // LDS position lane % CPR, holding k-chunk position ^ ((row / SW) % CPR).
-  const int lrow = lane / CPR, lpos = lane % CPR;
+  // This lane's chunk in load instruction i (RPI tile rows from row (wave * X_I + i) * RPI):
+  // BK = 64: row lane / 8 of the block, k-chunk (lane % 8) ^ ((row / 2) % 8);
+  // BK = 32: line L = lane / 8, h = (lane % 8) ^ L, row L + 8 * (h % 2), k-chunk h / 2.
+  const int lrow = BK == 32 ? ((lane >> 3) | (((lane & 7) ^ (lane >> 3)) & 1) << 3) : lane / CPR;
+  const int lkc = BK == 32 ? (((lane & 7) ^ (lane >> 3)) >> 1) : lane % CPR;
   int aoff[A_I], boff[B_I], akc[A_I], bkc[B_I];
 #pragma unroll
   for (int i = 0; i < A_I; ++i) {
     const int row = (wave * A_I + i) * RPI + lrow;
     aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
-    akc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+    akc[i] = (BK == 32 ? lkc : (lkc ^ ((row / SW) % CPR))) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_I; ++i) {
     const int row = (wave * B_I + i) * RPI + lrow;
     boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
-    bkc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
+    bkc[i] = (BK == 32 ? lkc : (lkc ^ ((row / SW) % CPR))) * 8;
   }
   // Loads of k-tile kt into stage st. Every step issues its loads, also past the last
   // k-tile (those read out of range: zeros, no memory traffic), so the number of loads
@@ -705,19 +711,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   }
 
   // Fragment reads: row (wm*TM + i*16 + lane%16) of A, k-chunk ks*4 + lane/16; the row's
-  // swizzle term depends on lane%16 only (fragment rows start at multiples of 16).
-  const int fsw = ((lane & 15) / SW) % CPR;
+  // swizzle term depends on lane%16 only (fragment rows start at multiples of 16), so a
+  // lane's element offset inside the fragment's 16 rows is fixed: fpos[ks].
+  int fpos[BK / 32];
+  if constexpr (BK == 32) {
+    const int L = lane & 7, h = ((lane >> 3) & 1) | ((lane >> 4) << 1);
+    fpos[0] = (L * 8 + (h ^ L)) * 8;
+  } else {
+    const int fsw = ((lane & 15) / SW) % CPR;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) fpos[ks] = (lane & 15) * BK + ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
+  }
   auto compute = [&](auto st) {
     const uint16_t* sa = stage_a(st);
     const uint16_t* sb = stage_b(st);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      const int pos = ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
+      const int pos = fpos[ks];
       bf16x8_t af[FM], wf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16 + (lane & 15)) * BK + pos];
+      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16) * BK + pos];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16 + (lane & 15)) * BK + pos];
+      for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16) * BK + pos];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll

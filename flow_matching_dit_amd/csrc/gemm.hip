@@ -761,156 +761,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane, PRE ? res : nullptr);
 }
 
-// Variant with the MFMA fragments double buffered in registers: while the MFMAs of
-// k-tile kt run from one register set, the fragments of k-tile kt + 1 are read from LDS
-// into the other, so the matrix cores do not wait for LDS within a step. LDS stage
-// kt % ST is refilled with k-tile kt + ST as soon as every wave has read it (one step
-// later), so ST - 1 tiles of loads are in flight while one is multiplied.
-template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma2_kernel(GemmArgs a, Epi e) {
-  constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int KSN = BK / 32;       // MFMA k steps per tile
-  constexpr int CPR = BK / 8;
-  constexpr int RPI = 64 / CPR;
-  constexpr int SW = 16 / CPR;
-  constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);
-  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-  static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
-  static_assert(ST == 3, "three stages (the step body is unrolled over 6 = lcm(3, 2) steps)");
-  constexpr int PER_STAGE = A_I + B_I;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * BK], As1[BM * BK], As2[BM * BK];
-  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BN * BK], Bs1[BN * BK], Bs2[BN * BK];
-  auto stage_a = [&](auto st) -> uint16_t* {
-    if constexpr (decltype(st)::value == 0) return As0;
-    else if constexpr (decltype(st)::value == 1) return As1;
-    else return As2;
-  };
-  auto stage_b = [&](auto st) -> uint16_t* {
-    if constexpr (decltype(st)::value == 0) return Bs0;
-    else if constexpr (decltype(st)::value == 1) return Bs1;
-    else return Bs2;
-  };
-
-  if (a.rows_dev) {
-    a.rows = min(a.rows, *a.rows_dev);
-    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
-  }
-  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of<GM>(nm, nn, tm, tn);
-  const int g = blockIdx.y;
-  const int split = blockIdx.z;
-  const int cat = a.ids ? a.ids[g] : 0;
-  const int r0 = tm * BM, n0 = tn * BN;
-  const int kbeg = split * a.k_per_split;
-  const int kend = min(a.K, kbeg + a.k_per_split);
-
-  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
-  const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
-  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * 2));
-
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int lrow = lane / CPR, lpos = lane % CPR;
-  int aoff[A_I], boff[B_I], akc[A_I], bkc[B_I];
-#pragma unroll
-  for (int i = 0; i < A_I; ++i) {
-    const int row = (wave * A_I + i) * RPI + lrow;
-    aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
-    akc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_I; ++i) {
-    const int row = (wave * B_I + i) * RPI + lrow;
-    boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
-    bkc[i] = (lpos ^ ((row / SW) % CPR)) * 8;
-  }
-  auto issue = [&](auto st, int kt) {
-    uint16_t* sa = stage_a(st);
-    uint16_t* sb = stage_b(st);
-    const int k0 = kbeg + kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_I; ++i)
-      dma16(ra_rsrc, sa + (wave * A_I + i) * 64 * 8,
-            (k0 + akc[i] < kend && aoff[i] != OOB) ? aoff[i] + (k0 + akc[i]) * 2 : OOB);
-#pragma unroll
-    for (int i = 0; i < B_I; ++i)
-      dma16(rw_rsrc, sb + (wave * B_I + i) * 64 * 8,
-            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + (k0 + bkc[i]) * 2 : OOB);
-  };
-
-  floatx4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  bf16x8_t fa[2][KSN][FM], fw[2][KSN][FN];
-  const int fsw = ((lane & 15) / SW) % CPR;
-  auto lds_read = [&](auto st, auto set) {
-    constexpr int R = decltype(set)::value;
-    const uint16_t* sa = stage_a(st);
-    const uint16_t* sb = stage_b(st);
-#pragma unroll
-    for (int ks = 0; ks < KSN; ++ks) {
-      const int pos = ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[R][ks][i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16 + (lane & 15)) * BK + pos];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fw[R][ks][j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16 + (lane & 15)) * BK + pos];
-    }
-  };
-  auto mfmas = [&](auto set) {
-    constexpr int R = decltype(set)::value;
-#pragma unroll
-    for (int ks = 0; ks < KSN; ++ks)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[R][ks][j], fa[R][ks][i], acc[i][j], 0, 0, 0);
-  };
-  // Step kt (U = kt % 6): stage kt + 1 landed (stage kt + 2 may still be in flight) and
-  // every wave is done with its reads of stage kt % 3 (made in step kt - 1); refill that
-  // stage with k-tile kt + 3, read the fragments of k-tile kt + 1, multiply k-tile kt.
-  const int nk = (kend - kbeg + BK - 1) / BK;
-  auto step = [&](auto u, int kt) {
-    constexpr int U = decltype(u)::value;
-    wait_vm_barrier<PER_STAGE>();
-    issue(ic<U % 3>{}, kt + 3);
-    if (kt + 1 < nk) lds_read(ic<(U + 1) % 3>{}, ic<(U + 1) % 2>{});
-    mfmas(ic<U % 2>{});
-  };
-
-  issue(ic<0>{}, 0);
-  issue(ic<1>{}, 1);
-  issue(ic<2>{}, 2);
-  wait_vm_barrier<2 * PER_STAGE>();
-  lds_read(ic<0>{}, ic<0>{});
-  int kt = 0;
-  for (; kt + 6 <= nk; kt += 6) {
-    step(ic<0>{}, kt);
-    step(ic<1>{}, kt + 1);
-    step(ic<2>{}, kt + 2);
-    step(ic<3>{}, kt + 3);
-    step(ic<4>{}, kt + 4);
-    step(ic<5>{}, kt + 5);
-  }
-  if (kt < nk) step(ic<0>{}, kt);
-  if (kt + 1 < nk) step(ic<1>{}, kt + 1);
-  if (kt + 2 < nk) step(ic<2>{}, kt + 2);
-  if (kt + 3 < nk) step(ic<3>{}, kt + 3);
-  if (kt + 4 < nk) step(ic<4>{}, kt + 4);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
-}
-
 // ------------------------------------------------------------------------------------
 // Skinny MFMA GEMM for <= 64 rows per group (weight streaming: B = 1 projections and
 // the per-embodiment linears). A workgroup owns 16 output columns; its NWAVE waves take

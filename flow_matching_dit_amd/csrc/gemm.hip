@@ -571,6 +571,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// XOR mask of the k-chunk position of tile row r (r % 16 given) for 128-byte rows.
+__device__ __forceinline__ int kswz64(int r) { return (r >> 1) & 7; }
+
 // f(ic<0>{}), f(ic<1>{}), ..., f(ic<N - 1>{}) in order (compile-time indices).
 template <typename F, int... I>
 __device__ __forceinline__ void for_seq_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -588,7 +591,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int CPR = BK / 8;       // 16-byte chunks per tile row
   constexpr int RPI = 64 / CPR;     // tile rows per wave load instruction
-  constexpr int SW = 16 / CPR;      // tile rows per 256 bytes of LDS
   constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);  // load instructions per wave and stage
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
   static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
@@ -662,13 +664,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   for (int i = 0; i < A_I; ++i) {
     const int row = (wave * A_I + i) * RPI + lrow;
     aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
-    akc[i] = (BK == 32 ? lkc : (lkc ^ ((row / SW) % CPR))) * 8;
+    if constexpr (BK == 32) akc[i] = lkc * 8;
+    else akc[i] = (lkc ^ kswz64(row & 15)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_I; ++i) {
     const int row = (wave * B_I + i) * RPI + lrow;
     boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
-    bkc[i] = (BK == 32 ? lkc : (lkc ^ ((row / SW) % CPR))) * 8;
+    if constexpr (BK == 32) bkc[i] = lkc * 8;
+    else bkc[i] = (lkc ^ kswz64(row & 15)) * 8;
   }
   // Loads of k-tile kt into stage st. Every step issues its loads, also past the last
   // k-tile (those read out of range: zeros, no memory traffic), so the number of loads
@@ -718,7 +722,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
     const int L = lane & 7, h = ((lane >> 3) & 1) | ((lane >> 4) << 1);
     fpos[0] = (L * 8 + (h ^ L)) * 8;
   } else {
-    const int fsw = ((lane & 15) / SW) % CPR;
+    const int fsw = kswz64(lane & 15);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) fpos[ks] = (lane & 15) * BK + ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
   }
@@ -1156,7 +1160,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     if (cfg == 0) return dma_kind<256, 256, 4, 4, 32, 4, 8>(a, e, splits, s);
     if (cfg == 1) return dma_kind<256, 128, 4, 4, 64, 3, 8>(a, e, splits, s);
     if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16>(a, e, splits, s);
-    if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 3, 16>(a, e, splits, s);
+    // 128 x 64 tiles: 24 steps of 64 k with little work each; a fourth stage keeps three
+    // tiles of loads in flight (measured 9% faster than three stages)
+    if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 4, 16>(a, e, splits, s);
   }
   switch (cfg == 5 ? 2 : cfg) {  // e4m3 weights: 64 x 128 tiles for narrow outputs too
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);

@@ -860,9 +860,10 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
 // than the weight stream itself. Instead the workgroup copies its rows into LDS once
 // (coalesced loads straight into LDS, rows padded by 16 bytes so that the 16 rows of a
 // fragment read fall on distinct bank groups), while each wave's weight loads for its
-// whole slice of K (at most KC k-steps) are already in flight.
+// whole slice of K (at most KC k-steps) are already in flight. LN: the rows are the fp32
+// residual stream instead, normalised (GemmArgs::ln) by the waves as they stage them.
 constexpr int SKL_MAX_LDS = 64 * 1024;
-template <int MF, int NC, int NWAVE, int EK>
+template <int MF, int NC, int NWAVE, int EK, bool LN = false>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a, Epi e) {
   constexpr int KC = 8;
   extern __shared__ __attribute__((aligned(1024))) uint16_t skl[];
@@ -893,12 +894,28 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
   }
   // 1. activation rows [0, rows) x [kbeg, kbeg + kper) -> LDS (chunk c: row c / cpr, k-chunk c % cpr;
   //    the padding chunk and k past kend read 0)
-  for (int j = wave; j * 64 < tc; j += NWAVE) {
-    const int c = j * 64 + lane;
-    const int row = c / cpr, kc = c - row * cpr;
-    const int k = kbeg + kc * 8;
-    const bool in = c < tc && kc < cpr - 1 && k < kend;
-    dma16(ra_rsrc, skl + j * 64 * 8, in ? (row * (int)a.lda + k) * 2 : OOB);
+  constexpr int LR = (MF * 16 + NWAVE - 1) / NWAVE, LV = 8;  // LN: rows per wave, float4 per lane
+  float4 xv[LN ? LR : 1][LN ? LV : 1];
+  if constexpr (LN) {  // rows wave, wave + NWAVE, ... of the fp32 residual stream, whole rows (kper = K)
+    const float* hr = (const float*)a.A;
+#pragma unroll
+    for (int r = 0; r < LR; ++r) {
+      const int row = wave + r * NWAVE;
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int c = 4 * lane + 256 * i;
+        xv[r][i] = (row < a.rows && c < a.K) ? *(const float4*)(hr + (long)row * a.lda + c)
+                                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+  } else {
+    for (int j = wave; j * 64 < tc; j += NWAVE) {
+      const int c = j * 64 + lane;
+      const int row = c / cpr, kc = c - row * cpr;
+      const int k = kbeg + kc * 8;
+      const bool in = c < tc && kc < cpr - 1 && k < kend;
+      dma16(ra_rsrc, skl + j * 64 * 8, in ? (row * (int)a.lda + k) * 2 : OOB);
+    }
   }
   // the weight loads below must be issued after these (the wait in 3. counts on it)
   asm volatile("" ::: "memory");
@@ -917,8 +934,48 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
     for (int c = 0; c < NC; ++c)
       wv[i][c] = buf_load16(rw_rsrc, (s0 + i < s1 && k < kend && woff[c] != OOB) ? woff[c] + k * 2 : OOB);
   }
-  // 3. the staged rows are complete (weight loads may still be in flight)
-  wait_vm_barrier<KC * NC>();
+  if constexpr (LN) {
+    // 1'. each row: mean and variance over its K values (the arithmetic of the residual
+    //     LayerNorm kernel, in the same order), normalised, modulated, bf16 into LDS
+#pragma unroll
+    for (int r = 0; r < LR; ++r) {
+      const int row = wave + r * NWAVE;
+      if (row >= a.rows) break;
+      float sm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < LV; ++i) sm += (xv[r][i].x + xv[r][i].y) + (xv[r][i].z + xv[r][i].w);
+      const float mean = wave_sum(sm) / (float)a.K;
+      float s2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        if (4 * lane + 256 * i < a.K) {
+          const float d0 = xv[r][i].x - mean, d1 = xv[r][i].y - mean, d2 = xv[r][i].z - mean, d3 = xv[r][i].w - mean;
+          s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+        }
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)a.K + 1e-5f);
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int c = 4 * lane + 256 * i;
+        if (c < a.K) {
+          float o[4] = {(xv[r][i].x - mean) * rstd, (xv[r][i].y - mean) * rstd, (xv[r][i].z - mean) * rstd,
+                        (xv[r][i].w - mean) * rstd};
+          if (a.ln_ada) {
+            const float4 sc = *(const float4*)(a.ln_ada + c);
+            const float4 sh = *(const float4*)(a.ln_ada + a.K + c);
+            o[0] = o[0] * (1.0f + sc.x) + sh.x;
+            o[1] = o[1] * (1.0f + sc.y) + sh.y;
+            o[2] = o[2] * (1.0f + sc.z) + sh.z;
+            o[3] = o[3] * (1.0f + sc.w) + sh.w;
+          }
+          *(uint2*)&skl[row * rs + c] = make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
+        }
+      }
+    }
+    __syncthreads();  // 3. the staged rows are complete (weight loads may still be in flight)
+  } else {
+    wait_vm_barrier<KC * NC>();  // 3. the staged rows are complete (weight loads may still be in flight)
+  }
   floatx4_t acc[NC][MF];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -971,11 +1028,11 @@ static size_t skinny_lds_bytes(const GemmArgs& a, int mf, int nc, int nwave) {
   return bytes <= SKL_MAX_LDS ? (size_t)bytes : 0;
 }
 
-template <int MF, int NC, int NWAVE>
+template <int MF, int NC, int NWAVE, bool LN = false>
 static hipError_t skinny_lds_kind(const GemmArgs& a, const Epi& e, int splits, size_t lds, hipStream_t s) {
   dim3 grid((a.N + 16 * NC - 1) / (16 * NC), a.groups, splits), blk(64 * NWAVE);
 #define GR00T_SKL_CASE(K) \
-  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K>), grid, blk, lds, s, a, e); break;
+  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K, LN>), grid, blk, lds, s, a, e); break;
   switch (e.kind) {
     GR00T_SKL_CASE(EPI_STORE)
     GR00T_SKL_CASE(EPI_RESID_ADD)
@@ -1136,6 +1193,14 @@ int gemm_mfma_splits(int rows, int N, int K, int groups) {
   return best;
 }
 
+bool gemm_ln_fits(int rows, int K, DType wt) {
+  if (rows < 1 || rows > 32 || wt != DT_BF16 || K < 1024 || K > 2048 || K % 256 != 0) return false;
+  GemmArgs a{};
+  a.rows = rows;
+  a.k_per_split = K;
+  return skinny_lds_bytes(a, rows <= 16 ? 1 : 2, 2, 8) != 0;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStream_t s) {
   GemmArgs a = a_in;
   if (a.rows <= 0 || a.N <= 0 || a.groups <= 0) return hipSuccess;
@@ -1149,6 +1214,14 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
   }
   a.k_per_split = a.K / splits;
   if ((long)a.rows * a.lda * 2 >= (1l << 31) || (long)a.N * a.K * 2 >= (1l << 31)) return hipErrorInvalidValue;
+  if (a.ln) {  // LayerNorm of the fp32 A rows folded into the skinny kernel
+    if (!gemm_ln_fits(a.rows, a.K, wt) || splits != 1 || a.groups != 1 || a.a_row_off != 0 || a.lda < a.K)
+      return hipErrorInvalidValue;
+    // 32 columns per workgroup: the rows held in registers allow one workgroup per CU, so
+    // half as many workgroups fit the chip in one round
+    const size_t lds = skinny_lds_bytes(a, a.rows <= 16 ? 1 : 2, 2, 8);
+    return a.rows <= 16 ? skinny_lds_kind<1, 2, 8, true>(a, e, 1, lds, s) : skinny_lds_kind<2, 2, 8, true>(a, e, 1, lds, s);
+  }
   if (a.rows <= 64) {
     if (a.rows <= 16) return skinny_go<1>(a, e, fp8, splits, s);
     if (a.rows <= 32) return skinny_go<2>(a, e, fp8, splits, s);

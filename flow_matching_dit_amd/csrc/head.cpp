@@ -499,12 +499,13 @@ hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType 
 }
 
 // h += A W^T + b for the residual stream h: direct residual add, or split-K into the
-// partial buffer (then *pend = number of partials the next norm must add).
-hipError_t resid_gemm(gr00t_head* h, const GemmArgs& a, DType at, DType wt, long pstride, int& pend, hipStream_t s) {
+// partial buffer (then *pend = number of partials the next norm must add). direct: never split.
+hipError_t resid_gemm(gr00t_head* h, const GemmArgs& a, DType at, DType wt, long pstride, int& pend, hipStream_t s,
+                      bool direct = false) {
   Epi e = ep_store(h->w.h, true, a.N);
   const bool mfma = at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 &&
                     a.N % 4 == 0;
-  const int splits = mfma ? gemm_mfma_splits(a.rows, a.N, a.K, a.groups) : 1;
+  const int splits = mfma && !direct ? gemm_mfma_splits(a.rows, a.N, a.K, a.groups) : 1;
   if (splits > 1) {
     e.kind = EPI_PARTIAL;
     e.out = h->w.part;
@@ -699,7 +700,19 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       LAUNCH(h, s, K_SMALL, launch_copy_rows(h->w.s, D, h->w.h, D, S, 0, B, D, s));
     }
     // ---- DiT blocks. The two residual GEMMs (o projection, MLP down) may run split-K
-    // into fp32 partials; the following norm adds them to h in a fixed order.
+    // into fp32 partials; the following norm adds them to h in a fixed order. With at most
+    // 32 rows (B = 1) the norm before the MLP is folded into the MLP-up GEMM instead (the
+    // skinny kernel normalises the fp32 rows of h as it stages them) and the o projection
+    // adds into h directly: one launch fewer per block.
+    const bool fold = A == DT_BF16 && dw == DT_BF16 && gemm_ln_fits((int)M, D, dw);
+    auto normed = [&](int N, const float* ada) {  // A operand of a GEMM that reads LN(h)
+      GemmArgs a = ga(fold ? (const void*)h->w.h : (const void*)h->w.n, D, (int)M, N, D);
+      if (fold) {
+        a.ln = 1;
+        a.ln_ada = ada;
+      }
+      return a;
+    };
     int pend = 0;  // partial sums not yet added to h
     const long pstride = M * D;
     for (int l = 0; l < Nl; ++l) {
@@ -758,12 +771,12 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         a.W = at<void>(h, lo.wo);
         a.bias = at<float>(h, lo.bo);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.so) : nullptr;
-        LAUNCH(h, s, K_O_PROJ, resid_gemm(h, a, A, dw, pstride, pend, s));
+        LAUNCH(h, s, K_O_PROJ, resid_gemm(h, a, A, dw, pstride, pend, s, fold));
       }
-      LAUNCH(h, s, K_NORM3, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, nullptr, s));
+      if (!fold) LAUNCH(h, s, K_NORM3, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, nullptr, s));
       pend = 0;
       {
-        GemmArgs a = ga(h->w.n, D, (int)M, F, D);
+        GemmArgs a = normed(F, nullptr);
         a.W = at<void>(h, lo.w1);
         a.bias = at<float>(h, lo.b1);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.s1) : nullptr;

@@ -37,6 +37,12 @@ struct GemmArgs {
   int groups;
   int k_per_split;      // set by the launcher
   const int* rows_dev;  // optional device row count (dense GEMMs): rows = min(rows, *rows_dev)
+  // Optional LayerNorm of the A rows, folded into the skinny bf16 kernel (gemm_ln_fits): A is
+  // then the fp32 residual stream [rows][K] (row stride lda); each row is normalised over its K
+  // values (eps 1e-5), multiplied by (1 + scale) and shifted when ln_ada = [scale K | shift K]
+  // is given, and rounded to bf16 as the GEMM stages it. One split only.
+  int ln;
+  const float* ln_ada;
 };
 
 struct Epi {
@@ -73,6 +79,10 @@ struct Epi {
 
 hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, const Epi& e, DType wt, hipStream_t s);
+// Whether a GEMM of `rows` rows and depth K with weights wt can take its A rows through the
+// folded LayerNorm (GemmArgs::ln): at most 32 rows, bf16 weights, 1024 <= K <= 2048, K a
+// multiple of 256, and the staged rows within the kernel's LDS budget.
+bool gemm_ln_fits(int rows, int K, DType wt);
 // K splits the MFMA GEMM would use for a split-K launch of this shape (1 = none).
 int gemm_mfma_splits(int rows, int N, int K, int groups);
 

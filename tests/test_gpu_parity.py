@@ -56,6 +56,12 @@ def test_small_width_parity(name, kw):
     _parity(small(name, **kw))
 
 
+def test_folded_layernorm_parity_b1():
+    # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
+    # and the residual projections add into h unsplit
+    _parity(small("dit32_bf16_b1", hidden=1536, num_heads=32, ff_dim=3072), flags=H.FLAG_USE_GRAPH, prepare=True)
+
+
 def test_wave_per_head_attention_parity():
     # 64 samples x 16 heads of width 48: at >= 1024 (sample, head) pairs attention runs one
     # wave per pair (ragged VL lengths, skipped key tiles); the oracle runs on sampled rows

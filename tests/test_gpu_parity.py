@@ -56,6 +56,13 @@ def test_small_width_parity(name, kw):
     _parity(small(name, **kw))
 
 
+def test_full_width_batch64_two_blocks_parity():
+    # 64 samples of 17 tokens at width 1536: every block GEMM runs at its full-size shape
+    # (1088 rows; the MLP down projection in 4 K-splits); the oracle checks 3 samples
+    _parity(small("dit32_bf16_b64", num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
+            flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 31, 63])
+
+
 def test_folded_layernorm_parity_b1():
     # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
     # and the residual projections add into h unsplit

@@ -63,6 +63,19 @@ def test_full_width_batch64_two_blocks_parity():
             flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 31, 63])
 
 
+@pytest.mark.parametrize("name,batch", [
+    ("dit32_bf16_b64", 2),    # 34 rows: skinny kernel, 4 row fragments, activations staged in LDS
+    ("dit32_bf16_b64", 4),    # 68 rows: 64 x 128 and 128 x 64 tiles, the MLP down in 8 K-splits
+    ("dit32_bf16_b64", 12),   # 204 rows: several row tiles, ragged last tile
+    ("dit32_fp8_b256", 1),    # e4m3 weights, 17 rows: skinny e4m3 kernel
+    ("dit32_fp8_b256", 4),    # e4m3 weights, 68 rows: register-staged e4m3 tiles
+])
+def test_full_width_mid_batch_parity(name, batch):
+    # the GEMM configurations between the B=1 and B=64 shapes, at the full width of 1536
+    _parity(small(name, batch=batch, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
+            flags=H.FLAG_USE_GRAPH, prepare=True)
+
+
 def test_folded_layernorm_parity_b1():
     # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
     # and the residual projections add into h unsplit

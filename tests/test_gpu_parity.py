@@ -76,6 +76,13 @@ def test_full_width_mid_batch_parity(name, batch):
             flags=H.FLAG_USE_GRAPH, prepare=True)
 
 
+def test_full_width_batch256_bf16_parity():
+    # 4352 rows: the MLP up and q,k,v projections take 256 x 256 tiles (GELU and head-major
+    # epilogues), the narrow projections 256 x 128; the oracle checks 3 samples
+    _parity(small("dit32_bf16_b64", batch=256, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
+            flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 101, 255])
+
+
 def test_folded_layernorm_parity_b1():
     # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
     # and the residual projections add into h unsplit

@@ -83,6 +83,17 @@ def test_full_width_batch256_bf16_parity():
             flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 101, 255])
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("dit32_bf16_b64", dict(batch=64, num_heads=16, hidden=768, ff_dim=1536)),  # one wave per pair
+    ("dit32_bf16_b1", {}),                                                        # workgroup per pair
+])
+def test_short_horizon_single_query_fragment_parity(name, kw):
+    # horizon 8: 9 tokens, one 16-query fragment per (sample, head) in both attention kernels
+    w = small(name, **kw)
+    w = replace(w, cfg=replace(w.cfg, action_horizon=8))
+    _parity(w, samples=[0, 63] if w.batch == 64 else None)
+
+
 def test_folded_layernorm_parity_b1():
     # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
     # and the residual projections add into h unsplit

@@ -133,6 +133,44 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
     return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1, prof_live
 
 
+# Horizon and step-count variants of the same 32-block model (the weights do not depend on
+# either): the base N1.7 horizon of 40 and K in {1, 2, 8, 16} Euler steps.
+VARIANTS = [("dit32_bf16_b1", 40, 4), ("dit32_bf16_b1", 16, 1), ("dit32_bf16_b1", 16, 2),
+            ("dit32_bf16_b1", 16, 8), ("dit32_bf16_b1", 16, 16), ("dit32_bf16_b64", 40, 4)]
+
+
+def variants_leg(weights, H, synth, calls=20):
+    """get_action p50 of each horizon / step-count variant (graph replays, inputs in HBM)."""
+    from dataclasses import replace
+
+    import torch
+    out = []
+    for name, hz, k in VARIANTS:
+        base = synth.WORKLOADS[name]
+        w = replace(base, name=f"{name}_h{hz}_k{k}", cfg=replace(base.cfg, action_horizon=hz, num_steps=k))
+        inputs, noise = synth.make_inputs(w), synth.make_noise(w)
+        h = H.Gr00tHead(w.cfg, max_batch=w.batch, max_vl_len=w.vl_len, flags=H.FLAG_USE_GRAPH)
+        h.load_weights(weights).finalize()
+        h.prepare(w.batch, w.vl_len)
+        d = H.device_inputs(inputs, noise, h.act_torch_dtype)
+        o = torch.empty((w.batch, hz, w.cfg.action_dim), dtype=torch.float32, device="cuda:0")
+        for _ in range(3):
+            h.get_action(**d, out=o)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(calls):
+            t = time.perf_counter()
+            h.get_action(**d, out=o)
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t) * 1e3)
+        h.close()
+        p50 = statistics.median(ts)
+        out.append({"workload": w.name, "batch": w.batch, "horizon": hz, "euler_steps": k, "p50_ms": round(p50, 4),
+                    "chunks_per_s": round(w.batch / p50 * 1e3, 1)})
+        log(f"[bench] variant {w.name}: p50 {p50:.3f} ms")
+    return out
+
+
 def stats(xs):
     xs = sorted(xs)
     return {"p50_ms": round(statistics.median(xs), 4), "mean_ms": round(statistics.fmean(xs), 4),
@@ -206,6 +244,8 @@ def main():
     ap.add_argument("--profile-calls", type=int, default=2)
     ap.add_argument("--cpu-samples", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the horizon 40 and K = 1, 2, 8, 16 variants (p50 per get_action)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -255,6 +295,8 @@ def main():
         "roofline": roof,
         "breakdown": breakdown,
     }
+    if args.variants:
+        result["variants"] = variants_leg(weights, H, synth)
     if not args.no_cpu_baseline:
         cpu, err = cpu_leg(args, w, weights, inputs, noise, first)
         result["cpu_baseline"] = cpu

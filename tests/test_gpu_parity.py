@@ -94,6 +94,19 @@ def test_short_horizon_single_query_fragment_parity(name, kw):
     _parity(w, samples=[0, 63] if w.batch == 64 else None)
 
 
+@pytest.mark.parametrize("name,hz,k", [
+    ("dit32_bf16_b1", 40, 4),    # the base N1.7 horizon: 41 tokens, three query fragments
+    ("dit32_bf16_b64", 40, 4),   # 2624 rows: 256 x 256 tiles for the MLP and q,k,v
+    ("dit32_bf16_b1", 16, 1),
+    ("dit32_bf16_b1", 16, 2),
+    ("dit32_bf16_b1", 16, 16),
+])
+def test_horizon_and_step_variants_parity(name, hz, k):
+    w = small(name, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144)
+    w = replace(w, cfg=replace(w.cfg, action_horizon=hz, num_steps=k))
+    _parity(w, flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 63] if w.batch == 64 else None)
+
+
 def test_folded_layernorm_parity_b1():
     # at most 32 rows and a width of 1024..2048: the norms run inside the GEMMs that read them
     # and the residual projections add into h unsplit

@@ -98,6 +98,20 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
     h.profile(False)
     log(f"[bench] {w.name}: {args.steps} calls in {total_s * 1e3:.1f} ms; per call p50 {statistics.median(per_call):.3f} ms")
 
+    # the same batch again with the VL key/value caches of the last full call reused (several
+    # action chunks drawn from one backbone output)
+    reuse = lambda: h.get_action_reuse_vl(w.batch, w.vl_len, d["state"], d["embodiment_id"], noise=d["noise"],
+                                          action_mask=d["action_mask"], out=out)
+    for _ in range(2):
+        reuse()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        reuse()
+    torch.cuda.synchronize()
+    reuse_s = (time.perf_counter() - t0) / args.steps
+    log(f"[bench] {w.name} reusing the VL caches: {reuse_s * 1e3:.3f} ms per call")
+
     # live launch timing of every kernel class (eager, HIP events on the call's stream)
     h.profile(True)
     for _ in range(args.profile_calls):
@@ -130,7 +144,7 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
         lat_wall.append((time.perf_counter() - t) * 1e3)
         lat_dev.append(e0.elapsed_time(e1))
     h.close()
-    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1, prof_live
+    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1, prof_live, reuse_s
 
 
 # Horizon and step-count variants of the same 32-block model (the weights do not depend on
@@ -275,8 +289,8 @@ def main():
     t = time.time()
     weights, inputs, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
     log(f"[bench] synthetic weights and inputs for {w.name} in {time.time() - t:.1f}s")
-    total_s, per_call, prof, first, lat_wall, lat_dev, prof_b1, prof_live = gpu_leg(args, w, weights, inputs, noise, H,
-                                                                                     synth)
+    total_s, per_call, prof, first, lat_wall, lat_dev, prof_b1, prof_live, reuse_s = gpu_leg(args, w, weights, inputs,
+                                                                                              noise, H, synth)
     value = w.batch * args.steps / total_s
     roof, breakdown = roofline(prof, w, inputs, args.profile_calls, prof_live)
     result = {
@@ -294,6 +308,9 @@ def main():
                        if lat_wall else None),
         "roofline": roof,
         "breakdown": breakdown,
+        "reuse_vl": {"ms_per_call": round(reuse_s * 1e3, 4), "chunks_per_s": round(w.batch / reuse_s, 2),
+                     "what": "gr00t_get_action_reuse_vl on the same batch: VL LayerNorm, key masks and K/V "
+                             "projection of the previous full call reused"},
     }
     if args.variants:
         result["variants"] = variants_leg(weights, H, synth)

@@ -142,6 +142,9 @@ struct gr00t_head {
   uint8_t* bad_host = nullptr;      // pinned copy of the per-sample bad-id flags
   hipEvent_t bad_event = nullptr;
   int bad_pending_B = 0;
+  // (B, L_pad) of the VL key/value caches and key masks in the workspace: those of the last
+  // call that ran the full prologue (0, 0: none yet)
+  int kv_B = 0, kv_L = 0;
   std::vector<int> tau;
   // launch timing (gr00t_profile_*)
   bool prof_on = false;
@@ -577,43 +580,50 @@ int build_tables(gr00t_head* h, hipStream_t s) {
 
 // ------------------------------------------------------------------ the launch sequence
 
-int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
+// reuse_vl: the VL part (key masks, VL LayerNorm, K/V projection) is skipped and the caches
+// of the last full prologue, for the same (B, L_pad), are used as they are.
+int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s, bool reuse_vl = false) {
   const gr00t_config& c = h->cfg;
   const int B = in->batch, L = in->vl_len, D = c.hidden, E = c.vl_dim, Nc = (c.num_layers + 1) / 2;
   const Layout& lay = h->lay;
   const DType A = h->act;
   const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
   const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
-  LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
   LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
-  // only VL tokens admitted by some block are normalised and projected: their row
-  // indices are compacted on the device (vrow[0 .. *vcount))
-  LAUNCH(h, s, K_SMALL, launch_compact_rows(h->w.code, B * L, h->w.vrow, h->w.vcount, s));
-  LAUNCH(h, s, K_VLLN, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
-                                        at<float>(h, lay.vlln_b), nullptr, s, h->w.vrow, h->w.vcount));
-  {  // keys and values of every cross block: [valid rows, E] x [Nc*2D, E]^T -> head-major caches
-    GemmArgs a = ga(h->w.vln, E, B * L, Nc * 2 * D, E);
-    a.rows_dev = h->w.vcount;
-    a.W = at<void>(h, lay.kv_w);
-    a.bias = at<float>(h, lay.kv_b);
-    a.wscale = kvw == DT_FP8 ? at<float>(h, lay.kv_s) : nullptr;
-    Epi e{};
-    e.kind = EPI_HEADS;
-    e.out_f32 = A == DT_F32;
-    e.heads[0] = h->w.kc;
-    e.heads[1] = h->w.vc;
-    e.nwhich = 2;
-    e.width = D;
-    e.nh = c.num_heads;
-    e.hd = c.head_dim;
-    e.pos_per_b = L;
-    const int Lp = round32(L);
-    e.pstride[0] = e.pstride[1] = Lp;
-    e.transposed[0] = 0;
-    e.transposed[1] = 1;  // values cached [L/32][hd][32] for the attention's V^T operand
-    e.layer_stride[0] = e.layer_stride[1] = (long)B * Lp * D;
-    e.row_map = h->w.vrow;
-    LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));
+  if (!reuse_vl) {
+    h->kv_B = h->kv_L = 0;  // no valid cache until the projection below is enqueued
+    LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
+    // only VL tokens admitted by some block are normalised and projected: their row
+    // indices are compacted on the device (vrow[0 .. *vcount))
+    LAUNCH(h, s, K_SMALL, launch_compact_rows(h->w.code, B * L, h->w.vrow, h->w.vcount, s));
+    LAUNCH(h, s, K_VLLN, launch_layernorm(in->vl_features, A, E, h->w.vln, A, E, B * L, E, at<float>(h, lay.vlln_g),
+                                          at<float>(h, lay.vlln_b), nullptr, s, h->w.vrow, h->w.vcount));
+    {  // keys and values of every cross block: [valid rows, E] x [Nc*2D, E]^T -> head-major caches
+      GemmArgs a = ga(h->w.vln, E, B * L, Nc * 2 * D, E);
+      a.rows_dev = h->w.vcount;
+      a.W = at<void>(h, lay.kv_w);
+      a.bias = at<float>(h, lay.kv_b);
+      a.wscale = kvw == DT_FP8 ? at<float>(h, lay.kv_s) : nullptr;
+      Epi e{};
+      e.kind = EPI_HEADS;
+      e.out_f32 = A == DT_F32;
+      e.heads[0] = h->w.kc;
+      e.heads[1] = h->w.vc;
+      e.nwhich = 2;
+      e.width = D;
+      e.nh = c.num_heads;
+      e.hd = c.head_dim;
+      e.pos_per_b = L;
+      const int Lp = round32(L);
+      e.pstride[0] = e.pstride[1] = Lp;
+      e.transposed[0] = 0;
+      e.transposed[1] = 1;  // values cached [L/32][hd][32] for the attention's V^T operand
+      e.layer_stride[0] = e.layer_stride[1] = (long)B * Lp * D;
+      e.row_map = h->w.vrow;
+      LAUNCH(h, s, K_KV_PROJ, gemm(h, a, e, A, kvw, s));
+    }
+    h->kv_B = B;
+    h->kv_L = L;
   }
   {  // state encoder: one token per sample
     GemmArgs a = ga(in->state, c.state_dim, 1, D, c.state_dim);
@@ -831,7 +841,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
   return GR00T_OK;
 }
 
-int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out) {
+int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out, bool reuse_vl = false) {
   if (!h) return GR00T_E_INVALID_ARG;
   if (!in) return fail(h, GR00T_E_INVALID_ARG, "inputs is NULL");
   if (!out) return fail(h, GR00T_E_INVALID_ARG, "output pointer is NULL");
@@ -841,10 +851,14 @@ int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out) {
   if (in->vl_len < 1 || in->vl_len > h->cfg.max_vl_len)
     return fail(h, GR00T_E_SHAPE, "vl_len " + std::to_string(in->vl_len) + " outside [1, max_vl_len=" +
                                       std::to_string(h->cfg.max_vl_len) + "]");
-  if (!in->vl_features) return fail(h, GR00T_E_INVALID_ARG, "vl_features is NULL");
+  if (!reuse_vl && !in->vl_features) return fail(h, GR00T_E_INVALID_ARG, "vl_features is NULL");
   if (!in->state) return fail(h, GR00T_E_INVALID_ARG, "state is NULL");
   if (!in->embodiment_id) return fail(h, GR00T_E_INVALID_ARG, "embodiment_id is NULL");
   if (!h->finalized) return fail(h, GR00T_E_NOT_FINALIZED, "handle is not finalized");
+  if (reuse_vl && (h->kv_B != in->batch || h->kv_L != in->vl_len))
+    return fail(h, GR00T_E_NO_VL_CACHE, "no VL key/value cache for (B=" + std::to_string(in->batch) + ", L=" +
+                                            std::to_string(in->vl_len) + "): the last full call had (B=" +
+                                            std::to_string(h->kv_B) + ", L=" + std::to_string(h->kv_L) + ")");
   return GR00T_OK;
 }
 
@@ -1048,8 +1062,8 @@ int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len) {
   return GR00T_OK;
 }
 
-int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream) {
-  int rc = check_inputs(h, in, action_pred);
+static int get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream, bool reuse_vl) {
+  int rc = check_inputs(h, in, action_pred, reuse_vl);
   if (rc != GR00T_OK) return rc;
   const bool use_graph = (h->cfg.flags & GR00T_FLAG_USE_GRAPH) != 0;
   const auto key = std::make_pair((int)in->batch, (int)in->vl_len);
@@ -1061,7 +1075,7 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
   HIPCHK(h, hipSetDevice(h->device));
   rc = pre_call_checks(h, in, s);
   if (rc != GR00T_OK) return rc;
-  rc = run_prologue(h, in, s);
+  rc = run_prologue(h, in, s, reuse_vl);
   if (rc != GR00T_OK) return rc;
   if (have_graph) {
     LAUNCH(h, s, K_GRAPH, hipGraphLaunch(h->graphs[key], s));
@@ -1076,6 +1090,14 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, 
   h->bad_pending_B = in->batch;
   h->calls++;
   return GR00T_OK;
+}
+
+int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream) {
+  return get_action(h, in, action_pred, hip_stream, false);
+}
+
+int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream) {
+  return get_action(h, in, action_pred, hip_stream, true);
 }
 
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v, void* hip_stream) {

@@ -23,11 +23,12 @@ STATUS = {
     0: "OK", -1: "E_INVALID_ARG", -2: "E_SHAPE", -3: "E_EMBODIMENT", -4: "E_NOT_FINALIZED",
     -5: "E_UNKNOWN_WEIGHT", -6: "E_UNCAPTURED", -7: "E_HIP", -8: "E_OOM", -9: "E_MISSING_WEIGHT",
     -10: "E_DEVICE_ERROR",
+    -11: "E_NO_VL_CACHE",
 }
 
 # Every exported symbol of include/gr00t_head.h.
 EXPORTS = ("gr00t_create", "gr00t_load_weights", "gr00t_finalize", "gr00t_prepare", "gr00t_get_action",
-           "gr00t_velocity", "gr00t_destroy", "gr00t_last_error", "gr00t_device_bytes",
+           "gr00t_get_action_reuse_vl", "gr00t_velocity", "gr00t_destroy", "gr00t_last_error", "gr00t_device_bytes",
            "gr00t_profile_enable", "gr00t_profile_read", "gr00t_profile_class_name")
 
 
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gr00t_prepare.restype = c_int
     lib.gr00t_get_action.argtypes = [c_void_p, POINTER(Gr00tInputs), c_void_p, c_void_p]
     lib.gr00t_get_action.restype = c_int
+    lib.gr00t_get_action_reuse_vl.argtypes = [c_void_p, POINTER(Gr00tInputs), c_void_p, c_void_p]
+    lib.gr00t_get_action_reuse_vl.restype = c_int
     lib.gr00t_velocity.argtypes = [c_void_p, POINTER(Gr00tInputs), c_int32, c_void_p, c_void_p]
     lib.gr00t_velocity.restype = c_int
     lib.gr00t_destroy.argtypes = [c_void_p]
@@ -178,6 +181,19 @@ class Gr00tHead:
                            state_features_out)
         self._check(self.lib.gr00t_get_action(self.h, ctypes.byref(inp), c_void_p(out.data_ptr()),
                                               self._stream(stream)))
+        return out
+
+    def get_action_reuse_vl(self, batch: int, vl_len: int, state, embodiment_id, noise=None, action_mask=None,
+                            out=None, state_features_out=None, stream=None):
+        """get_action with the VL key/value caches of the last full call of this (batch, vl_len)."""
+        import torch
+        if out is None:
+            out = torch.empty((batch, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
+                              device=state.device)
+        inp = Gr00tInputs(batch, vl_len, None, None, None, _ptr(state), _ptr(embodiment_id), _ptr(noise),
+                          _ptr(action_mask), _ptr(state_features_out))
+        self._check(self.lib.gr00t_get_action_reuse_vl(self.h, ctypes.byref(inp), c_void_p(out.data_ptr()),
+                                                       self._stream(stream)))
         return out
 
     def velocity(self, vl_features, vl_mask, image_mask, state, embodiment_id, noise, step_k: int,

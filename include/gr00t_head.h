@@ -42,7 +42,8 @@ typedef enum gr00t_status {
   GR00T_E_HIP = -7,            /* a HIP runtime call failed (message names it) */
   GR00T_E_OOM = -8,            /* device allocation failed */
   GR00T_E_MISSING_WEIGHT = -9, /* finalize with a weight never loaded */
-  GR00T_E_DEVICE_ERROR = -10   /* a previous call met an invalid id in non-strict mode */
+  GR00T_E_DEVICE_ERROR = -10,  /* a previous call met an invalid id in non-strict mode */
+  GR00T_E_NO_VL_CACHE = -11    /* reuse_vl call without a full call of the same (B, L_pad) */
 } gr00t_status;
 
 typedef enum gr00t_dtype {
@@ -158,6 +159,21 @@ int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len);
  */
 int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
                      void* hip_stream);
+
+/*
+ * get_action for a call whose vision-language input equals that of the last full
+ * get_action (or velocity) call on the handle: System 1 runs at a higher rate than the
+ * VLM that feeds it ("GR00T & Embodied AI Models", Dual-system architecture), so several
+ * action chunks are drawn from one backbone output. The VL LayerNorm, the key masks and
+ * the key/value projection of every cross block are not recomputed: the caches of that
+ * call are used as they are. in->vl_features, vl_mask and image_mask are not read (may
+ * be NULL); batch and vl_len must equal that call's; state, embodiment_id, noise and
+ * action_mask are this call's own. The result equals that of gr00t_get_action with the
+ * earlier call's VL inputs. Errors as gr00t_get_action, and E_NO_VL_CACHE when no full
+ * call of this (B, L_pad) precedes it (any full call of another shape replaces the cache).
+ */
+int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
+                              void* hip_stream);
 
 /* Debug and test entry: the velocity v(x = noise, tau_k) of Euler step `step_k`
  * ([B, H, A] f32, device), without integration or action_mask. inputs.noise must

@@ -138,6 +138,21 @@ def test_get_action_validates_before_device_work():
     h.close()
 
 
+def test_reuse_vl_validates_before_device_work():
+    lib = H.load_library()
+    h = H.Gr00tHead(synth.TINY, max_batch=2, max_vl_len=32)
+    out = ctypes.c_void_p(0x2000)
+    novl = _fake_inputs(1, 8)
+    novl.vl_features = None
+    assert lib.gr00t_get_action(h.h, ctypes.byref(novl), out, None) == -1  # a full call reads the VL input
+    assert lib.gr00t_get_action_reuse_vl(h.h, ctypes.byref(novl), out, None) == -4  # ... a reuse call does not
+    assert b"not finalized" in lib.gr00t_last_error(h.h)
+    assert lib.gr00t_get_action_reuse_vl(h.h, ctypes.byref(_fake_inputs(3, 8)), out, None) == -2
+    assert lib.gr00t_get_action_reuse_vl(h.h, ctypes.byref(_fake_inputs(1, 8)), None, None) == -1
+    assert lib.gr00t_get_action_reuse_vl(None, ctypes.byref(_fake_inputs(1, 8)), out, None) == -1
+    h.close()
+
+
 def test_destroy_null_and_last_error_null():
     lib = H.load_library()
     lib.gr00t_destroy(None)

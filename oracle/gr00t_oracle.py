@@ -31,7 +31,9 @@ final norm carry no affine; attention has no mask besides the key mask and no
 positional term; an empty key set gives a zero output; the feed-forward is
 Linear -> exact-erf GELU -> Linear; the per-embodiment MLPs use ReLU; only the
 H action rows are decoded; the vision-language LayerNorm (vlln) has gain and
-bias; action_mask multiplies the final chunk only.
+bias; action_mask multiplies the final chunk only. Training forward: the loss is
+the elementwise squared error times action_mask, summed, over the mask's sum plus
+1e-6; the training timestep bucket is floor(t * buckets) in float32.
 
 Parity: pinned by closed forms and invariants in tests/test_oracle.py; the
 whole network has no printed worked example on the pages, so beyond those pins
@@ -372,6 +374,51 @@ def get_action(cfg, weights, inputs, noise, params=None, return_velocity_at=None
     if inputs.get("action_mask") is not None:
         x = x * np.asarray(inputs["action_mask"], np.float64)
     return x
+
+
+def flow_interp(actions, noise, t):
+    """Noisy trajectory of flow-matching training [MODEL Flow matching diffusion, Training;
+    ARCH Training objective]: x_t = (1 - t) * noise + t * action, t [B] broadcast over (H, A)."""
+    t = np.asarray(t, np.float64)[:, None, None]
+    return (1.0 - t) * np.asarray(noise, np.float64) + t * np.asarray(actions, np.float64)
+
+
+def discretize_t(t, buckets: int = 1000) -> np.ndarray:
+    """Training timestep bucket floor(t * buckets) per sample (the inference grid's
+    discretisation applied to a continuous t), decided in float32."""
+    t32 = np.asarray(t, np.float32)
+    return np.floor(t32 * np.float32(buckets)).astype(np.int64)
+
+
+def training_loss(cfg, weights, inputs, actions, noise, t, params=None):
+    """Flow-matching training forward and loss [MODEL Flow matching diffusion, Training;
+    ARCH Training objective]. The draws are inputs: t [B] (t ~ Beta(1.5, 1) on the pages)
+    and noise [B,H,A] (N(0,1)).
+
+    x_t = (1 - t) noise + t action; target velocity v = action - noise; v_pred = the head's
+    velocity at x_t and the sample's bucket floor(t * buckets) (samples are independent, so
+    each runs with its own timestep); loss = sum(mask (v_pred - v)^2) / (sum(mask) + 1e-6)
+    with mask = action_mask (ones if absent). Returns (loss, v_pred)."""
+    P = params if params is not None else effective_params(cfg, weights)
+    vl_raw = effective_vl(cfg, inputs["vl_features"])
+    B, L, _ = vl_raw.shape
+    vl = layer_norm(vl_raw, P["vlln.gamma"], P["vlln.beta"])
+    valid = (np.ones((B, L), bool) if inputs.get("vl_mask") is None
+             else np.asarray(inputs["vl_mask"]).astype(bool))
+    image = (None if inputs.get("image_mask") is None
+             else np.asarray(inputs["image_mask"]).astype(bool))
+    ids = np.asarray(inputs["embodiment_id"]).astype(np.int64)
+    s = state_encoder(P, np.asarray(inputs["state"], np.float64), ids)
+    x_t = flow_interp(actions, noise, t)
+    v = np.asarray(actions, np.float64) - np.asarray(noise, np.float64)
+    tau = discretize_t(t, cfg["num_timestep_buckets"])
+    v_pred = np.concatenate([
+        velocity(P, cfg, vl[b:b + 1], valid[b:b + 1], None if image is None else image[b:b + 1],
+                 s[b:b + 1], x_t[b:b + 1], int(tau[b]), ids[b:b + 1]) for b in range(B)], axis=0)
+    mask = (np.ones_like(v) if inputs.get("action_mask") is None
+            else np.asarray(inputs["action_mask"], np.float64))
+    loss = float(np.sum(mask * (v_pred - v) ** 2) / (np.sum(mask) + 1e-6))
+    return loss, v_pred
 
 
 def state_features(cfg, weights, inputs, params=None):

@@ -383,3 +383,60 @@ def test_precisions_agree_roughly():
     for prec, tol in (("bf16", 2e-2), ("fp8", 5e-2)):
         w = tiny_workload(precision=prec)
         assert O.rel_l2(run(w), y32) < tol
+
+
+# ---------------------------------------------------------------- training forward
+
+def test_flow_interp_endpoints():
+    rng = np.random.default_rng(3)
+    a, n = rng.standard_normal((3, 4, 5)), rng.standard_normal((3, 4, 5))
+    x = O.flow_interp(a, n, np.array([0.0, 1.0, 0.5]))
+    assert np.array_equal(x[0], n[0])  # t = 0: pure noise
+    assert np.array_equal(x[1], a[1])  # t = 1: the action itself
+    assert np.allclose(x[2], (a[2] + n[2]) / 2, rtol=0, atol=1e-15)
+
+
+def test_training_bucket_matches_inference_grid():
+    for K in (1, 2, 4, 8, 16):
+        _, tau, _ = O.timestep_grid(K)
+        assert list(O.discretize_t(np.array([k / K for k in range(K)], np.float32))) == tau
+    assert list(O.discretize_t(np.array([0.0, 0.0005, 0.999, 1.0], np.float32))) == [0, 0, 999, 1000]
+
+
+def test_training_velocity_equals_inference_velocity_per_sample():
+    # each sample on a different point of the inference grid: the training forward at
+    # (x_t, t) is the inference velocity of that step evaluated at x = x_t
+    w = tiny_workload(num_steps=4)
+    wt, inp = synth.make_weights(w), synth.make_inputs(w)
+    rng = np.random.default_rng(5)
+    act = rng.standard_normal((w.batch, w.cfg.action_horizon, w.cfg.action_dim)).astype(np.float32)
+    noise = synth.make_noise(w)
+    ks = [3, 0, 2]
+    t = np.array([k / 4 for k in ks], np.float32)
+    _, v_pred = O.training_loss(w.cfg.as_dict(), wt, inp, act, noise, t)
+    x_t = O.flow_interp(act, noise, t)
+    for b, k in enumerate(ks):
+        v_inf = O.get_action(w.cfg.as_dict(), wt, inp, x_t, return_velocity_at=k)
+        assert np.allclose(v_pred[b], v_inf[b], rtol=0, atol=1e-12)
+
+
+def test_training_loss_closed_form():
+    # decoder output layer zeroed: v_pred is the per-category bias b2[id], so the loss is a
+    # plain masked mean of squared differences computed here independently
+    w = tiny_workload()
+    wt, inp = synth.make_weights(w), synth.make_inputs(w)
+    wt["action_dec.w2"][:] = 0
+    rng = np.random.default_rng(9)
+    act = rng.standard_normal((w.batch, w.cfg.action_horizon, w.cfg.action_dim)).astype(np.float32)
+    noise = synth.make_noise(w)
+    t = np.array([0.1, 0.6, 0.95], np.float32)
+    loss, v_pred = O.training_loss(w.cfg.as_dict(), wt, inp, act, noise, t)
+    b2 = wt["action_dec.b2"].astype(np.float64)[inp["embodiment_id"]][:, None, :]
+    assert np.allclose(v_pred, np.broadcast_to(b2, v_pred.shape), rtol=0, atol=1e-15)
+    mask = inp["action_mask"].astype(np.float64)
+    err = (b2 - (act.astype(np.float64) - noise.astype(np.float64))) ** 2
+    num = sum(float(mask[i, j, k] * err[i, j, k]) for i in range(err.shape[0])
+              for j in range(err.shape[1]) for k in range(err.shape[2]))
+    assert loss == pytest.approx(num / (float(mask.sum()) + 1e-6), rel=1e-12)
+    inp0 = dict(inp, action_mask=np.zeros_like(inp["action_mask"]))
+    assert O.training_loss(w.cfg.as_dict(), wt, inp0, act, noise, t)[0] == 0.0

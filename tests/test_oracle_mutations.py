@@ -98,6 +98,20 @@ def _velocity_decode_all_rows(P, cfg, vl, valid, image, s, x, tau, ids):
     return O.action_decoder(P, y[:, 1:, :], ids)
 
 
+def _interp_swapped(actions, noise, t):
+    t = np.asarray(t, np.float64)[:, None, None]
+    return t * np.asarray(noise, np.float64) + (1.0 - t) * np.asarray(actions, np.float64)
+
+
+def _bucket_rounded(t, buckets=1000):
+    return np.rint(np.asarray(t, np.float32) * np.float32(buckets)).astype(np.int64)
+
+
+def _training_target_sign(cfg, weights, inputs, actions, noise, t, params=None):
+    # the target velocity taken as noise - action
+    return O.__dict__["_orig_training_loss"](cfg, weights, inputs, noise, actions, 1.0 - np.asarray(t), params)
+
+
 CASES = [
     ("gelu", _gelu_tanh, pins.test_gelu_textbook_values),
     ("attention", _attention_no_temperature, pins.test_attention_temperature),
@@ -114,6 +128,9 @@ CASES = [
     ("sinusoid", _sinusoid_cos_first, pins.test_sinusoid_values),
     ("e4m3_encode", _e4m3_ties_away, pins.test_e4m3_roundtrip_all_codes_and_ties),
     ("velocity", _velocity_decode_all_rows, pins.test_horizon_permutation_equivariance),
+    ("flow_interp", _interp_swapped, pins.test_flow_interp_endpoints),
+    ("discretize_t", _bucket_rounded, pins.test_training_bucket_matches_inference_grid),
+    ("training_loss", _training_target_sign, pins.test_training_loss_closed_form),
 ]
 
 
@@ -122,6 +139,7 @@ def test_planted_mistake_is_caught(monkeypatch, name, bad, pin):
     monkeypatch.setitem(O.__dict__, "_orig_attention", O.attention)
     monkeypatch.setitem(O.__dict__, "_orig_block", O.transformer_block)
     monkeypatch.setitem(O.__dict__, "_orig_sinusoid", O.sinusoid)
+    monkeypatch.setitem(O.__dict__, "_orig_training_loss", O.training_loss)
     monkeypatch.setattr(O, name, bad)
     with pytest.raises(AssertionError):
         pin()

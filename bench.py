@@ -112,6 +112,23 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
     reuse_s = (time.perf_counter() - t0) / args.steps
     log(f"[bench] {w.name} reusing the VL caches: {reuse_s * 1e3:.3f} ms per call")
 
+    # flow-matching training forward and loss on the same batch (seeded draws: t ~ Beta(1.5, 1),
+    # actions ~ N(0, 1)); forward only
+    rng = np.random.default_rng(5)
+    acts = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).cuda()
+    tt = torch.from_numpy(rng.beta(1.5, 1.0, w.batch).astype(np.float32)).cuda()
+    train = lambda: h.train_forward(d["vl_features"], d["vl_mask"], d["image_mask"], d["state"], d["embodiment_id"],
+                                    acts, tt, d["noise"], action_mask=d["action_mask"], v_pred=False)
+    for _ in range(2):
+        train()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss = train()[0]
+    torch.cuda.synchronize()
+    train_s = (time.perf_counter() - t0) / args.steps
+    log(f"[bench] {w.name} training forward: {train_s * 1e3:.3f} ms per batch, loss {float(loss.item()):.4f}")
+
     # live launch timing of every kernel class (eager, HIP events on the call's stream)
     h.profile(True)
     for _ in range(args.profile_calls):
@@ -144,7 +161,7 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
         lat_wall.append((time.perf_counter() - t) * 1e3)
         lat_dev.append(e0.elapsed_time(e1))
     h.close()
-    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1, prof_live, reuse_s
+    return total_s, per_call, prof, first.cpu().numpy(), lat_wall, lat_dev, prof_b1, prof_live, reuse_s, train_s
 
 
 # Horizon and step-count variants of the same 32-block model (the weights do not depend on
@@ -289,8 +306,8 @@ def main():
     t = time.time()
     weights, inputs, noise = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
     log(f"[bench] synthetic weights and inputs for {w.name} in {time.time() - t:.1f}s")
-    total_s, per_call, prof, first, lat_wall, lat_dev, prof_b1, prof_live, reuse_s = gpu_leg(args, w, weights, inputs,
-                                                                                              noise, H, synth)
+    (total_s, per_call, prof, first, lat_wall, lat_dev, prof_b1, prof_live, reuse_s,
+     train_s) = gpu_leg(args, w, weights, inputs, noise, H, synth)
     value = w.batch * args.steps / total_s
     roof, breakdown = roofline(prof, w, inputs, args.profile_calls, prof_live)
     result = {
@@ -311,6 +328,9 @@ def main():
         "reuse_vl": {"ms_per_call": round(reuse_s * 1e3, 4), "chunks_per_s": round(w.batch / reuse_s, 2),
                      "what": "gr00t_get_action_reuse_vl on the same batch: VL LayerNorm, key masks and K/V "
                              "projection of the previous full call reused"},
+        "train_forward": {"ms_per_batch": round(train_s * 1e3, 4), "samples_per_s": round(w.batch / train_s, 2),
+                          "what": "gr00t_train_forward on the same batch: x_t, one DiT forward with per-sample "
+                                  "timesteps, masked MSE (forward only)"},
     }
     if args.variants:
         result["variants"] = variants_leg(weights, H, synth)

@@ -48,7 +48,7 @@ template <int EK, int NV>
 __device__ __forceinline__ void epi_store(const Epi& e, int g, int r, int n, float (&v)[NV], int cat, int split) {
   if (e.add_tab) {
 #pragma unroll
-    for (int q = 0; q < NV; ++q) v[q] += e.add_tab[(long)cat * e.add_cstride + n + q];
+    for (int q = 0; q < NV; ++q) v[q] += e.add_tab[(long)(e.add_by_group ? g : cat) * e.add_cstride + n + q];
   }
   if (EK != EPI_PARTIAL) {
 #pragma unroll

@@ -145,6 +145,12 @@ struct gr00t_head {
   // (B, L_pad) of the VL key/value caches and key masks in the workspace: those of the last
   // call that ran the full prologue (0, 0: none yet)
   int kv_B = 0, kv_L = 0;
+  // per-sample timestep tables of the training forward (allocated on its first call)
+  struct {
+    float *sin_t = nullptr, *tauemb = nullptr, *t1 = nullptr, *temb = nullptr, *stemb = nullptr, *ada = nullptr,
+          *c2 = nullptr;
+  } tr;
+  void* tr_base = nullptr;
   std::vector<int> tau;
   // launch timing (gr00t_profile_*)
   bool prof_on = false;
@@ -578,6 +584,69 @@ int build_tables(gr00t_head* h, hipStream_t s) {
   return GR00T_OK;
 }
 
+// Per-sample timestep tables of the training forward ("GR00T model class", Flow matching
+// diffusion, Training): the bucket floor(t_b * buckets) of each sample, its timestep
+// embedding, the adaLN [scale | shift] of every block and of the output norm, and the
+// timestep term of the action encoder's second linear under the sample's category. The
+// GEMM sequence is that of build_tables with one row per sample instead of one per step.
+int build_sample_tables(gr00t_head* h, const float* t, int B, hipStream_t s) {
+  const gr00t_config& c = h->cfg;
+  const int D = c.hidden, Nl = c.num_layers, T = c.time_freq_dim;
+  const Layout& L = h->lay;
+  const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
+  if (!h->tr_base) {
+    const size_t Bm = c.max_batch;
+    const size_t n_sin = Bm * T, n_d = Bm * D, n_ada = Bm * (size_t)(Nl + 1) * 2 * D;
+    const size_t total = n_sin + 5 * n_d + n_ada;
+    if (hipMalloc(&h->tr_base, total * sizeof(float)) != hipSuccess) {
+      h->tr_base = nullptr;
+      (void)hipGetLastError();
+      return fail(h, GR00T_E_OOM, "training tables: device allocation failed");
+    }
+    float* p = (float*)h->tr_base;
+    h->tr.sin_t = p;
+    p += n_sin;
+    h->tr.tauemb = p;
+    p += n_d;
+    h->tr.t1 = p;
+    p += n_d;
+    h->tr.temb = p;
+    p += n_d;
+    h->tr.stemb = p;
+    p += n_d;
+    h->tr.c2 = p;
+    p += n_d;
+    h->tr.ada = p;
+  }
+  HIPCHK(h, launch_sinusoid_t(t, B, c.num_timestep_buckets, T, h->tr.sin_t, s));
+  HIPCHK(h, launch_sinusoid_t(t, B, c.num_timestep_buckets, D, h->tr.tauemb, s));
+  GemmArgs a = ga(h->tr.sin_t, T, B, D, T);
+  a.W = at<void>(h, L.t_w1);
+  a.bias = at<float>(h, L.t_b1);
+  HIPCHK(h, launch_gemm_valu(a, ep_store(h->tr.t1, true, D, ACT_SILU), DT_F32, mw, s));
+  a = ga(h->tr.t1, D, B, D, D);
+  a.W = at<void>(h, L.t_w2);
+  a.bias = at<float>(h, L.t_b2);
+  HIPCHK(h, launch_gemm_valu(a, ep_store(h->tr.temb, true, D), DT_F32, mw, s));
+  HIPCHK(h, launch_silu(h->tr.temb, h->tr.stemb, (long)B * D, s));
+  a = ga(h->tr.stemb, D, B, (Nl + 1) * 2 * D, D);
+  a.W = at<void>(h, L.ada_w);
+  a.bias = at<float>(h, L.ada_b);
+  HIPCHK(h, launch_gemm_valu(a, ep_store(h->tr.ada, true, (long)(Nl + 1) * 2 * D), DT_F32, mw, s));
+  a = ga(h->tr.tauemb, D, 1, D, D);  // one row per sample, the sample's category
+  a.groups = B;
+  a.a_gstride = 1;
+  a.ids = h->w.ids;
+  a.W = at<void>(h, L.ae_w2t);
+  a.w_cstride = (long)D * D;
+  a.bias = at<float>(h, L.ae_b2);
+  a.b_cstride = D;
+  Epi e = ep_store(h->tr.c2, true, D);
+  e.out_gstride = 1;
+  HIPCHK(h, launch_gemm_valu(a, e, DT_F32, mw, s));
+  return GR00T_OK;
+}
+
 // ------------------------------------------------------------------ the launch sequence
 
 // reuse_vl: the VL part (key masks, VL LayerNorm, K/V projection) is skipped and the caches
@@ -657,7 +726,9 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s, bool reus
 }
 
 // Enqueue Euler steps [k0, k1). euler = false writes v of step k0 to w.vout instead.
-int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream_t s) {
+// per_sample: one forward with every sample's own timestep tables (h->tr: adaLN modulation
+// [B][N+1][2D] and the action encoder's timestep term [B][D]) instead of step k0's.
+int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream_t s, bool per_sample = false) {
   const gr00t_config& c = h->cfg;
   const int D = c.hidden, F = c.ff_dim, H = c.action_horizon, S = H + 1, Adim = c.action_dim, Nl = c.num_layers;
   const int C = c.num_categories, nh = c.num_heads, hd = c.head_dim;
@@ -670,7 +741,13 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
   const int Sp = round32(S);
   const size_t ab = act_bytes(h);
   (void)C;
+  const int ada_rows = per_sample ? S : 0;
+  const long ada_stride = per_sample ? (long)(Nl + 1) * 2 * D : 0;
   for (int k = k0; k < k1; ++k) {
+    // [scale | shift] of block l (l = Nl: the output norm)
+    auto ada_of = [&](int l) -> const float* {
+      return per_sample ? h->tr.ada + (size_t)l * 2 * D : h->w.ada + ((size_t)k * (Nl + 1) + l) * 2 * D;
+    };
     // ---- action encoder: a = W1 x + b1; z = swish(W2a a + [W2t tau_emb + b2]); h[1:] = W3 z + b3
     {
       GemmArgs a = ga(h->w.x, Adim, H, D, Adim);
@@ -692,8 +769,9 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       a.w_cstride = (long)D * D;
       e = ep_store(h->w.e2, f32, D, ACT_SILU);
       e.out_gstride = H;
-      e.add_tab = h->w.c2tab + (size_t)k * c.num_categories * D;
+      e.add_tab = per_sample ? h->tr.c2 : h->w.c2tab + (size_t)k * c.num_categories * D;
       e.add_cstride = D;
+      e.add_by_group = per_sample ? 1 : 0;
       LAUNCH(h, s, K_ACTION_ENC, gemm(h, a, e, A, mw, s));
       a = ga(h->w.e2, D, H, D, D);
       a.groups = B;
@@ -728,8 +806,8 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     for (int l = 0; l < Nl; ++l) {
       const LayerOff& lo = lay.L[l];
       const bool self = (l % 2) == 1;
-      const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + l) * 2 * D;
-      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada_of(l), s,
+                                                   ada_rows, ada_stride));
       pend = 0;
       {
         GemmArgs a = ga(h->w.n, D, (int)M, (self ? 3 : 1) * D, D);
@@ -800,8 +878,8 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     }
     // ---- output adaLN + projection, then decoder and Euler update
     {
-      const float* ada = h->w.ada + ((size_t)k * (Nl + 1) + Nl) * 2 * D;
-      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada, s));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada_of(Nl), s,
+                                                   ada_rows, ada_stride));
       GemmArgs a = ga(h->w.n, D, (int)M, D, D);
       a.W = at<void>(h, lay.p_w);
       a.bias = at<float>(h, lay.p_b);
@@ -1100,6 +1178,34 @@ int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* acti
   return get_action(h, in, action_pred, hip_stream, true);
 }
 
+int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t, float* loss,
+                        float* v_pred, void* hip_stream) {
+  int rc = check_inputs(h, in, loss);
+  if (rc != GR00T_OK) return rc;
+  if (!actions || !t) return fail(h, GR00T_E_INVALID_ARG, "actions and t are required");
+  if (!in->noise) return fail(h, GR00T_E_INVALID_ARG, "the training forward needs inputs.noise");
+  const gr00t_config& c = h->cfg;
+  const int B = in->batch, per = c.action_horizon * c.action_dim;
+  hipStream_t s = (hipStream_t)hip_stream;
+  HIPCHK(h, hipSetDevice(h->device));
+  rc = pre_call_checks(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  rc = run_prologue(h, in, s);  // VL, ids, state token (its x = noise is replaced below)
+  if (rc != GR00T_OK) return rc;
+  rc = build_sample_tables(h, t, B, s);
+  if (rc != GR00T_OK) return rc;
+  LAUNCH(h, s, K_SMALL, launch_flow_interp(actions, in->noise, t, h->w.x, B, per, s));
+  rc = run_steps(h, B, in->vl_len, 0, 1, false, s, true);
+  if (rc != GR00T_OK) return rc;
+  LAUNCH(h, s, K_SMALL, launch_masked_mse(h->w.vout, actions, in->noise, in->action_mask, h->w.bad, B, per, loss, s));
+  if (v_pred) HIPCHK(h, hipMemcpyAsync(v_pred, h->w.vout, sizeof(float) * B * per, hipMemcpyDeviceToDevice, s));
+  HIPCHK(h, hipMemcpyAsync(h->bad_host, h->w.bad, B, hipMemcpyDeviceToHost, s));
+  HIPCHK(h, hipEventRecord(h->bad_event, s));
+  h->bad_pending_B = B;
+  h->calls++;
+  return GR00T_OK;
+}
+
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v, void* hip_stream) {
   int rc = check_inputs(h, in, v);
   if (rc != GR00T_OK) return rc;
@@ -1130,6 +1236,7 @@ void gr00t_destroy(gr00t_head* h) {
   if (h->bad_event) (void)hipEventDestroy(h->bad_event);
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   if (h->bad_host) (void)hipHostFree(h->bad_host);
+  if (h->tr_base) (void)hipFree(h->tr_base);
   if (h->arena || h->wsbase) (void)hipDeviceSynchronize();
   if (h->arena) (void)hipFree(h->arena);
   if (h->wsbase) (void)hipFree(h->wsbase);

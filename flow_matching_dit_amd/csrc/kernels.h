@@ -53,8 +53,9 @@ struct Epi {
   long out_ld;          // row stride of out (elements)
   long out_gstride;     // rows between groups
   int out_row_off;
-  const float* add_tab; // optional per-category row added before the activation
+  const float* add_tab; // optional row added before the activation: row cat (or g, add_by_group)
   long add_cstride;
+  int add_by_group;     // 1: add_tab row = group index g instead of the group's category
   // EPI_HEADS: column n -> section sec = n / width, which = sec % nwhich,
   // layer = sec / nwhich, head = (n % width) / hd, d = n % hd; row r -> (b, pos) with
   // pos_per_b positions per sample; element goes to heads[which] + layer * layer_stride[which] +
@@ -100,8 +101,11 @@ hipError_t launch_compact_rows(const uint8_t* code, int n, int* idx, int* count,
 // Residual add of split-K partial sums, then adaLN / LayerNorm:
 //   h[r] += sum_s partials[s][r]  (fixed order, written back), y = LN(h[r]) [* (1 + scale) + shift]
 // partials may be NULL (nsplit = 0): then it is launch_layernorm on fp32 h.
+// ada_rows > 0: row r takes its modulation from ada + (r / ada_rows) * ada_stride (one
+// [scale | shift] per sample of ada_rows rows); 0: every row uses ada.
 hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y,
-                                  DType yt, int rows, int D, const float* ada, hipStream_t s);
+                                  DType yt, int rows, int D, const float* ada, hipStream_t s, int ada_rows = 0,
+                                  long ada_stride = 0);
 
 // Multi-head attention per (sample, head): softmax(q k^T / sqrt(hd)) v.
 // q [B][nh][S][hd]; k [B][nh][Lp][hd] (keys row-major, Lp = Lk rounded up to 32);
@@ -139,6 +143,15 @@ hipError_t launch_output(const float* x, const uint8_t* mask, const uint8_t* bad
                          int per, hipStream_t s);
 // tab[k][i] = sinusoid(tau[k]) of width dim: [sin(tau w_i) | cos(tau w_i)], w_i = 10000^(-i/half).
 hipError_t launch_sinusoid(const int* tau_host_k, int K, int dim, float* tab, hipStream_t s);
+// tab[b] = sinusoid (as launch_sinusoid) of the bucket floor(t[b] * buckets), decided in fp32, b < n.
+hipError_t launch_sinusoid_t(const float* t, int n, int buckets, int dim, float* tab, hipStream_t s);
+// x[b, i] = (1 - t[b]) * noise[b, i] + t[b] * actions[b, i], per values per sample.
+hipError_t launch_flow_interp(const float* actions, const float* noise, const float* t, float* x, int B, int per,
+                              hipStream_t s);
+// loss[0] = sum(mask * (v_pred - (actions - noise))^2) / (sum(mask) + 1e-6) over B * per values (mask NULL:
+// ones), summed in double in a fixed order (one workgroup); NaN if bad[b] != 0 for some sample.
+hipError_t launch_masked_mse(const float* v_pred, const float* actions, const float* noise, const uint8_t* mask,
+                             const uint8_t* bad, int B, int per, float* loss, hipStream_t s);
 // y = SiLU(x), n floats.
 hipError_t launch_silu(const float* x, float* y, long n, hipStream_t s);
 // fp32 -> act dtype copy of n elements.

@@ -84,11 +84,13 @@ hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt
 template <typename TY, int NS>
 __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict__ h, const float* __restrict__ part,
                                                               long split_stride, TY* __restrict__ y, int rows, int D,
-                                                              const float* __restrict__ ada) {
+                                                              const float* __restrict__ ada_base, int ada_rows,
+                                                              long ada_stride) {
   constexpr int MAXV = 8;  // float4 per lane: 8 * 4 * 64 = 2048 columns
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
+  const float* ada = ada_base ? ada_base + (ada_rows > 0 ? (long)(row / ada_rows) * ada_stride : 0) : nullptr;
   float* hr = h + (long)row * D;
   float4 v[MAXV];
   float s = 0.0f;
@@ -148,30 +150,32 @@ __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict_
 
 template <typename TY>
 static hipError_t resid_ln_go(float* h, const float* partials, int nsplit, long split_stride, TY* y, int rows, int D,
-                              const float* ada, hipStream_t s) {
+                              const float* ada, int ada_rows, long ada_stride, hipStream_t s) {
   dim3 grid((rows + 3) / 4), blk(256);
   switch (nsplit) {
-    case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 1: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 1>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 2: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 2>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 3: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 3>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 4: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 4>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 5: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 5>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 6: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 6>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 7: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 7>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
-    case 8: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 8>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada); break;
+    case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 1: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 1>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 2: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 2>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 3: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 3>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 4: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 4>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 5: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 5>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 6: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 6>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 7: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 7>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 8: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 8>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y, DType yt,
-                                  int rows, int D, const float* ada, hipStream_t s) {
+                                  int rows, int D, const float* ada, hipStream_t s, int ada_rows, long ada_stride) {
   if (rows <= 0) return hipSuccess;
-  if (D > 2048 || (D % 4) != 0) return hipErrorInvalidValue;
+  if (D > 2048 || (D % 4) != 0 || ada_rows < 0) return hipErrorInvalidValue;
   if (!partials) nsplit = 0;
-  if (yt == DT_F32) return resid_ln_go<float>(h, partials, nsplit, split_stride, (float*)y, rows, D, ada, s);
-  if (yt == DT_BF16) return resid_ln_go<bf16>(h, partials, nsplit, split_stride, (bf16*)y, rows, D, ada, s);
+  if (yt == DT_F32)
+    return resid_ln_go<float>(h, partials, nsplit, split_stride, (float*)y, rows, D, ada, ada_rows, ada_stride, s);
+  if (yt == DT_BF16)
+    return resid_ln_go<bf16>(h, partials, nsplit, split_stride, (bf16*)y, rows, D, ada, ada_rows, ada_stride, s);
   return hipErrorInvalidValue;
 }
 
@@ -805,6 +809,80 @@ hipError_t launch_sinusoid(const int* tau_host_k, int K, int dim, float* tab, hi
   TauList t;
   for (int k = 0; k < 64; ++k) t.v[k] = k < K ? tau_host_k[k] : 0;
   hipLaunchKernelGGL(sinusoid_kernel, dim3(K), dim3(256), 0, s, t, dim, tab);
+  return hipGetLastError();
+}
+
+// Flow-matching training ("GR00T model class", Flow matching diffusion, Training; "Model
+// architecture", Training objective): per-sample timestep sinusoids, the noisy trajectory
+// and the masked squared-error loss.
+__global__ void sinusoid_t_kernel(const float* t, int buckets, int dim, float* tab) {
+  const int b = blockIdx.x;
+  const int tau = (int)floorf(t[b] * (float)buckets);  // the bucket, decided in fp32
+  const int half = dim / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double w = pow(10000.0, -(double)i / (double)half);
+    const double arg = (double)tau * w;
+    tab[(long)b * dim + i] = (float)sin(arg);
+    tab[(long)b * dim + half + i] = (float)cos(arg);
+  }
+}
+
+hipError_t launch_sinusoid_t(const float* t, int n, int buckets, int dim, float* tab, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sinusoid_t_kernel, dim3(n), dim3(256), 0, s, t, buckets, dim, tab);
+  return hipGetLastError();
+}
+
+__global__ void flow_interp_kernel(const float* a, const float* z, const float* t, float* x, int per, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float tb = t[i / per];
+  x[i] = (1.0f - tb) * z[i] + tb * a[i];
+}
+
+hipError_t launch_flow_interp(const float* actions, const float* noise, const float* t, float* x, int B, int per,
+                              hipStream_t s) {
+  const long n = (long)B * per;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(flow_interp_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, actions, noise, t, x,
+                     per, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void masked_mse_kernel(const float* vp, const float* a, const float* z,
+                                                          const uint8_t* mask, const uint8_t* bad, int B, long n,
+                                                          float* loss) {
+  __shared__ double sn[1024], sd[1024];
+  const int t = threadIdx.x;
+  double num = 0.0, den = 0.0;
+  for (long i = t; i < n; i += 1024) {  // each thread in index order, then a fixed tree
+    const double m = mask ? (double)mask[i] : 1.0;
+    const double d = (double)vp[i] - ((double)a[i] - (double)z[i]);
+    num += m * d * d;
+    den += m;
+  }
+  sn[t] = num;
+  sd[t] = den;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) {
+      sn[t] += sn[t + w];
+      sd[t] += sd[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    int anybad = 0;
+    for (int b = 0; b < B; ++b) anybad |= bad ? bad[b] : 0;
+    loss[0] = anybad ? __builtin_nanf("") : (float)(sn[0] / (sd[0] + 1e-6));
+  }
+}
+
+hipError_t launch_masked_mse(const float* v_pred, const float* actions, const float* noise, const uint8_t* mask,
+                             const uint8_t* bad, int B, int per, float* loss, hipStream_t s) {
+  if (B <= 0 || per <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(masked_mse_kernel, dim3(1), dim3(1024), 0, s, v_pred, actions, noise, mask, bad, B,
+                     (long)B * per, loss);
   return hipGetLastError();
 }
 

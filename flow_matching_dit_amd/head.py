@@ -28,8 +28,9 @@ STATUS = {
 
 # Every exported symbol of include/gr00t_head.h.
 EXPORTS = ("gr00t_create", "gr00t_load_weights", "gr00t_finalize", "gr00t_prepare", "gr00t_get_action",
-           "gr00t_get_action_reuse_vl", "gr00t_velocity", "gr00t_destroy", "gr00t_last_error", "gr00t_device_bytes",
-           "gr00t_profile_enable", "gr00t_profile_read", "gr00t_profile_class_name")
+           "gr00t_get_action_reuse_vl", "gr00t_train_forward", "gr00t_velocity", "gr00t_destroy",
+           "gr00t_last_error", "gr00t_device_bytes", "gr00t_profile_enable", "gr00t_profile_read",
+           "gr00t_profile_class_name")
 
 
 class Gr00tConfig(ctypes.Structure):
@@ -77,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gr00t_get_action.restype = c_int
     lib.gr00t_get_action_reuse_vl.argtypes = [c_void_p, POINTER(Gr00tInputs), c_void_p, c_void_p]
     lib.gr00t_get_action_reuse_vl.restype = c_int
+    lib.gr00t_train_forward.argtypes = [c_void_p, POINTER(Gr00tInputs), c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p]
+    lib.gr00t_train_forward.restype = c_int
     lib.gr00t_velocity.argtypes = [c_void_p, POINTER(Gr00tInputs), c_int32, c_void_p, c_void_p]
     lib.gr00t_velocity.restype = c_int
     lib.gr00t_destroy.argtypes = [c_void_p]
@@ -195,6 +199,19 @@ class Gr00tHead:
         self._check(self.lib.gr00t_get_action_reuse_vl(self.h, ctypes.byref(inp), c_void_p(out.data_ptr()),
                                                        self._stream(stream)))
         return out
+
+    def train_forward(self, vl_features, vl_mask, image_mask, state, embodiment_id, actions, t, noise,
+                      action_mask=None, v_pred=True, stream=None):
+        """(loss [1] f32, v_pred [B, H, A] f32 or None) of the flow-matching training forward."""
+        import torch
+        B = int(vl_features.shape[0])
+        loss = torch.empty(1, dtype=torch.float32, device=vl_features.device)
+        vp = (torch.empty((B, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
+                          device=vl_features.device) if v_pred else None)
+        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask, None)
+        self._check(self.lib.gr00t_train_forward(self.h, ctypes.byref(inp), _ptr(actions), _ptr(t),
+                                                 c_void_p(loss.data_ptr()), _ptr(vp), self._stream(stream)))
+        return loss, vp
 
     def velocity(self, vl_features, vl_mask, image_mask, state, embodiment_id, noise, step_k: int,
                  stream=None):

@@ -175,6 +175,27 @@ int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
 int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
                               void* hip_stream);
 
+/*
+ * Flow-matching training forward and loss of one batch ("GR00T model class", Flow matching
+ * diffusion, Training; "Model architecture", Training objective). The draws are inputs:
+ * t [B] f32 in [0, 1] (t ~ Beta(1.5, 1) on the pages) and inputs.noise [B, H, A] f32 (N(0, 1)).
+ *   x_t    = (1 - t) * noise + t * actions,     v = actions - noise
+ *   v_pred = the head's velocity at x_t for each sample's timestep bucket floor(t * buckets)
+ *            (the bucket decided in fp32; the timestep embedding, adaLN modulation and the
+ *            action encoder's timestep term are computed per sample)
+ *   loss   = sum(mask * (v_pred - v)^2) / (sum(mask) + 1e-6), mask = inputs.action_mask
+ *            (ones when NULL), summed in double in a fixed order
+ * actions [B, H, A] f32, loss [1] f32 and the optional v_pred [B, H, A] f32 are device
+ * pointers. Forward only (no gradients). Enqueued on `hip_stream` like gr00t_get_action,
+ * not captured in a graph; the first call allocates the per-sample tables
+ * (max_batch * ((num_layers + 1) * 2 * hidden + 6 * hidden + time_freq_dim) floats, freed by
+ * gr00t_destroy). Errors as gr00t_get_action, E_INVALID_ARG without actions, t or
+ * inputs.noise, E_OOM if the tables cannot be allocated. In non-strict mode an invalid id
+ * makes the loss NaN.
+ */
+int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t,
+                        float* loss, float* v_pred, void* hip_stream);
+
 /* Debug and test entry: the velocity v(x = noise, tau_k) of Euler step `step_k`
  * ([B, H, A] f32, device), without integration or action_mask. inputs.noise must
  * not be NULL. Same stream semantics as gr00t_get_action. */

@@ -153,6 +153,19 @@ def test_reuse_vl_validates_before_device_work():
     h.close()
 
 
+def test_train_forward_validates_before_device_work():
+    lib = H.load_library()
+    h = H.Gr00tHead(synth.TINY, max_batch=2, max_vl_len=32)
+    loss = ctypes.c_void_p(0x2000)
+    act, t = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    inp = _fake_inputs(1, 8)
+    assert lib.gr00t_train_forward(h.h, ctypes.byref(inp), act, t, None, None, None) == -1  # no loss output
+    assert lib.gr00t_train_forward(h.h, ctypes.byref(inp), None, t, loss, None, None) == -4  # not finalized first
+    assert lib.gr00t_train_forward(h.h, ctypes.byref(_fake_inputs(3, 8)), act, t, loss, None, None) == -2
+    assert lib.gr00t_train_forward(None, ctypes.byref(inp), act, t, loss, None, None) == -1
+    h.close()
+
+
 def test_destroy_null_and_last_error_null():
     lib = H.load_library()
     lib.gr00t_destroy(None)

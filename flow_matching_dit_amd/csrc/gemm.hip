@@ -565,6 +565,20 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// XOR mask of the 16-byte chunk position of e4m3 weight row r (CW chunks per row): with it
+// the 8-byte fragment reads of 16 consecutive rows by 32 lanes touch 64 distinct banks.
+template <int CW>
+__device__ __forceinline__ int wswz8(int r) { return CW == 4 ? (r >> 2) & 3 : (r >> 3) & 1; }
+
+// Eight e4m3 codes -> eight bf16 (exact), four gfx950 conversion instructions.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint2 w) {
+  const uint32_t v0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+  const uint32_t v1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+  const uint32_t v2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+  const uint32_t v3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  return __builtin_bit_cast(bf16x8_t, make_uint4(v0, v1, v2, v3));
+}
+
 // XOR mask of the k-chunk position of tile row r (r % 16 given) for 128-byte rows.
 __device__ __forceinline__ int kswz64(int r) { return (r >> 1) & 7; }
 
@@ -578,16 +592,25 @@ __device__ __forceinline__ void for_seq(F&& f) {
   for_seq_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM>
+// W8: the weights are e4m3 bytes [N][K] (one fp32 scale per column, applied in the epilogue).
+// Their tiles go into LDS as bytes (CW 16-byte chunks per BK-byte row) and each 8-value
+// fragment is decoded to bf16 after its LDS read (four conversion instructions). When a stage
+// has fewer weight load instructions than waves, the waves without one load out of range
+// (zeros, no memory traffic) into a spare chunk after the stage, so that every wave issues
+// the same loads and the wait counts stay exact.
+template <int BM, int BN, int WM, int WN, int BK, int ST, int EK, int GM, bool W8 = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi e) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int CPR = BK / 8;       // 16-byte chunks per tile row
+  constexpr int CPR = BK / 8;       // 16-byte chunks per bf16 tile row
   constexpr int RPI = 64 / CPR;     // tile rows per wave load instruction
-  constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);  // load instructions per wave and stage
+  constexpr int CW = W8 ? BK / 16 : CPR, RW = 64 / CW;  // weight rows: chunks per row, rows per instruction
+  constexpr int NWI = BN / RW;      // weight load instructions per stage
+  constexpr int A_I = BM / (RPI * NW), B_I = W8 ? (NWI + NW - 1) / NW : BN / (RPI * NW);
   static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-  static_assert(A_I * RPI * NW == BM && B_I * RPI * NW == BN, "tile rows must split evenly over the waves");
+  static_assert(A_I * RPI * NW == BM && (W8 ? NWI * RW == BN : B_I * RPI * NW == BN),
+                "tile rows must split evenly over the waves");
   static_assert(FM >= 1 && FN >= 1, "tile shape");
   static_assert(ST >= 2 && ST <= 6, "2 to 6 stages");
   constexpr int PER_STAGE = A_I + B_I;
@@ -599,9 +622,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * BK], As1[BM * BK];
   __shared__ __attribute__((aligned(1024))) uint16_t As2[ST > 2 ? BM * BK : 8], As3[ST > 3 ? BM * BK : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t As4[ST > 4 ? BM * BK : 8], As5[ST > 5 ? BM * BK : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BN * BK], Bs1[BN * BK];
-  __shared__ __attribute__((aligned(1024))) uint16_t Bs2[ST > 2 ? BN * BK : 8], Bs3[ST > 3 ? BN * BK : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t Bs4[ST > 4 ? BN * BK : 8], Bs5[ST > 5 ? BN * BK : 8];
+  constexpr int SB = W8 ? (BN * BK + 1024) / 2 : BN * BK;  // weight stage, 16-bit units (e4m3: bytes + spare)
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs0[SB], Bs1[SB];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs2[ST > 2 ? SB : 8], Bs3[ST > 3 ? SB : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs4[ST > 4 ? SB : 8], Bs5[ST > 5 ? SB : 8];
   auto stage_a = [&](auto st) -> uint16_t* {
     constexpr int V = decltype(st)::value;
     if constexpr (V == 0) return As0;
@@ -642,7 +666,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
   const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
   const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
-  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * (W8 ? 1 : 2)));
 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
@@ -661,12 +685,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
     if constexpr (BK == 32) akc[i] = lkc * 8;
     else akc[i] = (lkc ^ kswz64(row & 15)) * 8;
   }
+  int bdst[B_I];
 #pragma unroll
   for (int i = 0; i < B_I; ++i) {
-    const int row = (wave * B_I + i) * RPI + lrow;
-    boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
-    if constexpr (BK == 32) bkc[i] = lkc * 8;
-    else bkc[i] = (lkc ^ kswz64(row & 15)) * 8;
+    if constexpr (W8) {
+      // e4m3 row r keeps 16-byte chunk c at position c ^ wswz8(r): the 16-row fragment reads
+      // (8 bytes per lane) then fall on distinct banks
+      const int ii = i * NW + wave, row = ii * RW + lane / CW;
+      boff[i] = (ii < NWI && n0 + row < a.N) ? (n0 + row) * a.K : OOB;
+      bkc[i] = ((lane % CW) ^ wswz8<CW>(row)) * 16;  // element (= byte) offset in the k-tile
+      bdst[i] = min(ii, NWI) * 512;
+    } else {
+      const int row = (wave * B_I + i) * RPI + lrow;
+      boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K * 2 : OOB;
+      if constexpr (BK == 32) bkc[i] = lkc * 8;
+      else bkc[i] = (lkc ^ kswz64(row & 15)) * 8;
+      bdst[i] = (wave * B_I + i) * 64 * 8;
+    }
   }
   // Loads of k-tile kt into stage st. Every step issues its loads, also past the last
   // k-tile (those read out of range: zeros, no memory traffic), so the number of loads
@@ -681,8 +716,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
             (k0 + akc[i] < kend && aoff[i] != OOB) ? aoff[i] + (k0 + akc[i]) * 2 : OOB);
 #pragma unroll
     for (int i = 0; i < B_I; ++i)
-      dma16(rw_rsrc, sb + (wave * B_I + i) * 64 * 8,
-            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + (k0 + bkc[i]) * 2 : OOB);
+      dma16(rw_rsrc, sb + bdst[i],
+            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + (k0 + bkc[i]) * (W8 ? 1 : 2) : OOB);
   };
 
   floatx4_t acc[FM][FN];
@@ -692,7 +727,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // residual add: this lane's residual values are loaded now (the oldest loads in flight),
   // so the epilogue does not wait for them (wave tiles of up to 8 fragments: more would spill)
-  constexpr bool PRE = EK == EPI_RESID_ADD && FM * FN <= 8;
+  constexpr bool PRE = EK == EPI_RESID_ADD && FM * FN <= 8 && !W8;  // (W8: the decode needs the registers)
   float4 res[PRE ? FM * FN : 1];
   if constexpr (PRE) {
 #pragma unroll
@@ -720,6 +755,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) fpos[ks] = (lane & 15) * BK + ((ks * 4 + (lane >> 4)) ^ fsw) * 8;
   }
+  // e4m3 fragment reads: lane holds k = 32 ks + 8 (lane / 16) .. +7 of row lane % 16
+  int fpos8[BK / 32];
+#pragma unroll
+  for (int ks = 0; ks < BK / 32; ++ks) {
+    const int r16 = lane & 15, g = lane >> 4, c = (32 * ks + 8 * g) / 16;
+    fpos8[ks] = r16 * BK + ((c ^ wswz8<CW>(r16)) * 16) + (g & 1) * 8;
+  }
   auto compute = [&](auto st) {
     const uint16_t* sa = stage_a(st);
     const uint16_t* sb = stage_b(st);
@@ -730,7 +772,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)&sa[(wm * TM + i * 16) * BK + pos];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16) * BK + pos];
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (W8)
+          wf[j] = e4m3x8_to_bf16x8(*(const uint2*)((const uint8_t*)sb + (wn * TN + j * 16) * BK + fpos8[ks]));
+        else
+          wf[j] = *(const bf16x8_t*)&sb[(wn * TN + j * 16) * BK + pos];
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1126,13 +1173,13 @@ static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, int splits,
 //   2: 64x128, 4 waves, BK 64                    (fewer tiles: D-wide outputs, split-K)
 //   3: 32x64, 4 waves                            (<= 32 rows)
 //   4: 16x64, 4 waves                            (<= 16 rows)
-template <int BM, int BN, int WM, int WN, int BK, int ST, int GM>
+template <int BM, int BN, int WM, int WN, int BK, int ST, int GM, bool W8 = false>
 static hipError_t dma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
   dim3 grid(nm * nn, a.groups, splits);
   dim3 blk(64 * WM * WN);
 #define GR00T_DMA_CASE(K) \
-  case K: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, BK, ST, K, GM>), grid, blk, 0, s, a, e); break;
+  case K: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, BK, ST, K, GM, W8>), grid, blk, 0, s, a, e); break;
   switch (e.kind) {
     GR00T_DMA_CASE(EPI_STORE)
     GR00T_DMA_CASE(EPI_RESID_ADD)
@@ -1230,6 +1277,12 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     // 128 x 64 tiles: 24 steps of 64 k with little work each; a fourth stage keeps three
     // tiles of loads in flight (measured 9% faster than three stages)
     if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 4, 16>(a, e, splits, s);
+  } else {  // e4m3 weights: the same tiles, weight bytes into LDS, decoded per fragment
+    // 256 x 128 also where bf16 takes 256 x 256: with the decode, 64 x 64 wave tiles exceed
+    // the 128 registers of four waves per SIMD
+    if (cfg == 0 || cfg == 1) return dma_kind<256, 128, 4, 4, 64, 3, 8, true>(a, e, splits, s);
+    if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16, true>(a, e, splits, s);
+    if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 4, 16, true>(a, e, splits, s);
   }
   switch (cfg == 5 ? 2 : cfg) {  // e4m3 weights: 64 x 128 tiles for narrow outputs too
     case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);

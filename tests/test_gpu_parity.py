@@ -68,12 +68,13 @@ def test_full_width_batch64_two_blocks_parity():
     ("dit32_bf16_b64", 4),    # 68 rows: 64 x 128 and 128 x 64 tiles, the MLP down in 8 K-splits
     ("dit32_bf16_b64", 12),   # 204 rows: several row tiles, ragged last tile
     ("dit32_fp8_b256", 1),    # e4m3 weights, 17 rows: skinny e4m3 kernel
-    ("dit32_fp8_b256", 4),    # e4m3 weights, 68 rows: register-staged e4m3 tiles
+    ("dit32_fp8_b256", 4),    # e4m3 weights, 68 rows: 64 x 128 tiles of weight bytes
+    ("dit32_fp8_b256", 64),   # e4m3 weights, 1088 rows: 256 x 128 and 128 x 64 tiles, split-K MLP down
 ])
 def test_full_width_mid_batch_parity(name, batch):
     # the GEMM configurations between the B=1 and B=64 shapes, at the full width of 1536
     _parity(small(name, batch=batch, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
-            flags=H.FLAG_USE_GRAPH, prepare=True)
+            flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 40, 63] if batch == 64 else None)
 
 
 def test_full_width_batch256_bf16_parity():

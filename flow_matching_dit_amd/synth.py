@@ -49,7 +49,7 @@ class HeadConfig:
     num_timestep_buckets: int = 1000
     attend_text_every_n_blocks: int = 2
     time_freq_dim: int = 256
-    precision: str = "bf16"  # "fp32" | "bf16" | "fp8" (fp8 = e4m3 DiT matrices)
+    precision: str = "bf16"  # "fp32" | "bf16" | "fp8" (e4m3 DiT matrices) | "fp8a8" (and e4m3 inputs)
 
     def as_dict(self) -> dict:
         return asdict(self)
@@ -95,6 +95,9 @@ WORKLOADS["dit32_bf16_b16_h64"] = Workload("dit32_bf16_b16_h64", 3,
                                            batch=16, vl_len=1024, id_range=(0, 7))
 WORKLOADS["dit32_fp8_b256"] = Workload("dit32_fp8_b256", 4, _full_model(precision="fp8"),
                                        batch=256, vl_len=300, id_range=(0, 31))
+# W8A8 variant of the high-batch workload: e4m3 DiT weights and per-row e4m3 GEMM inputs
+WORKLOADS["dit32_w8a8_b256"] = Workload("dit32_w8a8_b256", 5, _full_model(precision="fp8a8"),
+                                        batch=256, vl_len=300, id_range=(0, 31))
 WORKLOAD_BY_INDEX = list(WORKLOADS.values())
 
 

@@ -33,7 +33,9 @@ Linear -> exact-erf GELU -> Linear; the per-embodiment MLPs use ReLU; only the
 H action rows are decoded; the vision-language LayerNorm (vlln) has gain and
 bias; action_mask multiplies the final chunk only. Training forward: the loss is
 the elementwise squared error times action_mask, summed, over the mask's sum plus
-1e-6; the training timestep bucket is floor(t * buckets) in float32.
+1e-6; the training timestep bucket is floor(t * buckets) in float32. W8A8 mode
+("fp8a8"): the input rows of every e4m3-weight GEMM are quantised to e4m3 per row
+(scale = row amax / 448), the code decided in float32 from the oracle's own value.
 
 Parity: pinned by closed forms and invariants in tests/test_oracle.py; the
 whole network has no printed worked example on the pages, so beyond those pins
@@ -117,6 +119,18 @@ def quantize_e4m3_columns(w32: np.ndarray):
     return deq, codes, scale
 
 
+def quantize_e4m3_rows(x) -> np.ndarray:
+    """Per-row e4m3 activations of the W8A8 mode ("fp8a8"): the input rows of a GEMM with
+    e4m3 weights. scale[r] = fp32(max_k |x[r,k]|) / fp32(448) (fp32 division; 1 for an all-zero
+    row), code = e4m3(fp32(x / scale)) decided on fp32 operands, dequantised x = decode(code) *
+    scale: the column quantisation of the weights applied along the rows."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1, keepdims=True).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = e4m3_encode((x32 / scale).astype(np.float32))
+    return e4m3_decode(codes) * scale.astype(np.float64)
+
+
 # --------------------------------------------------------------------------
 # Building blocks
 # --------------------------------------------------------------------------
@@ -162,6 +176,14 @@ def sinusoid(tau, dim: int) -> np.ndarray:
 
 def linear(x, w, b):
     return x @ w + b
+
+
+def dit_linear(cfg, x, w, b):
+    """A linear whose weight is an e4m3 matrix in the fp8 modes (is_fp8_matrix); in the W8A8
+    mode ("fp8a8") its input rows are quantised to e4m3 first (quantize_e4m3_rows)."""
+    if cfg["precision"] == "fp8a8":
+        x = quantize_e4m3_rows(x)
+    return linear(x, w, b)
 
 
 def category_linear(x, W, b, ids):
@@ -239,17 +261,17 @@ def transformer_block(P, cfg, l, h, vl, key_masks, temb):
     n = ada_layer_norm(P, p, h, temb)
     out = np.empty_like(h)
     for b in range(B):
-        q = linear(n[b], P[p + "attn.wq"], P[p + "attn.bq"]).reshape(S, nh, hd)
+        q = dit_linear(cfg, n[b], P[p + "attn.wq"], P[p + "attn.bq"]).reshape(S, nh, hd)
         if l % 2 == 1:
             src, admitted = n[b], np.ones(S, bool)
         else:
             src, admitted = vl[b], key_masks[b]
-        k = linear(src, P[p + "attn.wk"], P[p + "attn.bk"]).reshape(-1, nh, hd)
-        v = linear(src, P[p + "attn.wv"], P[p + "attn.bv"]).reshape(-1, nh, hd)
+        k = dit_linear(cfg, src, P[p + "attn.wk"], P[p + "attn.bk"]).reshape(-1, nh, hd)
+        v = dit_linear(cfg, src, P[p + "attn.wv"], P[p + "attn.bv"]).reshape(-1, nh, hd)
         out[b] = attention(q, k, v, admitted).reshape(S, D)
-    h = h + linear(out, P[p + "attn.wo"], P[p + "attn.bo"])
-    u = gelu(linear(layer_norm(h), P[p + "ff.w1"], P[p + "ff.b1"]))
-    return h + linear(u, P[p + "ff.w2"], P[p + "ff.b2"])
+    h = h + dit_linear(cfg, out, P[p + "attn.wo"], P[p + "attn.bo"])
+    u = gelu(dit_linear(cfg, layer_norm(h), P[p + "ff.w1"], P[p + "ff.b1"]))
+    return h + dit_linear(cfg, u, P[p + "ff.w2"], P[p + "ff.b2"])
 
 
 def dit(P, cfg, sa_embs, vl, valid, image, temb):
@@ -263,7 +285,7 @@ def dit(P, cfg, sa_embs, vl, valid, image, temb):
                                       None if image is None else image[b]) for b in range(B)]
         h = transformer_block(P, cfg, l, h, vl, masks, temb)
     y = ada_layer_norm(P, "out.", h, temb)
-    return linear(y, P["out.proj.w"], P["out.proj.b"])
+    return dit_linear(cfg, y, P["out.proj.w"], P["out.proj.b"])
 
 
 def state_encoder(P, state, ids):
@@ -332,7 +354,7 @@ def effective_params(cfg, weights: Dict[str, np.ndarray], threads: int = 8) -> D
         name, w = item
         if prec == "fp32":
             return name, np.asarray(w, dtype=np.float64)
-        if prec == "fp8" and is_fp8_matrix(name):
+        if prec in ("fp8", "fp8a8") and is_fp8_matrix(name):
             return name, quantize_e4m3_columns(w)[0]
         return name, round_bf16(w)
 

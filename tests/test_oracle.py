@@ -440,3 +440,44 @@ def test_training_loss_closed_form():
     assert loss == pytest.approx(num / (float(mask.sum()) + 1e-6), rel=1e-12)
     inp0 = dict(inp, action_mask=np.zeros_like(inp["action_mask"]))
     assert O.training_loss(w.cfg.as_dict(), wt, inp0, act, noise, t)[0] == 0.0
+
+
+# ---------------------------------------------------------------- W8A8 (per-row e4m3 GEMM inputs)
+
+def test_row_quantisation():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((4, 40)) * np.array([[0.01], [1.0], [300.0], [5e4]])
+    x[2, 7] = -1234.5  # this row's amax element is negative
+    q = O.quantize_e4m3_rows(x)
+    x32 = x.astype(np.float32)
+    for r in range(4):
+        scale = np.float32(np.max(np.abs(x32[r]))) / np.float32(448.0)
+        k = int(np.argmax(np.abs(x32[r])))
+        # the amax element takes the largest finite code, of its sign
+        assert q[r, k] == np.sign(x32[r, k]) * 448.0 * np.float64(scale)
+        # every value is its row's scale times an e4m3 value
+        assert np.all(np.isin(np.abs(q[r]) / np.float64(scale), O._E4M3_POS))
+    assert np.array_equal(O.quantize_e4m3_rows(np.zeros((2, 5))), np.zeros((2, 5)))
+    # rows whose amax is 448 (scale 1) of e4m3-representable values are unchanged
+    v = O._E4M3_POS[rng.integers(0, 127, size=(3, 30))] * rng.choice([-1.0, 1.0], size=(3, 30))
+    v[:, 0] = 448.0
+    assert np.array_equal(O.quantize_e4m3_rows(v), v)
+
+
+def test_w8a8_linear_is_exact_on_representable_operands():
+    # inputs and weights on the e4m3 grid with row / column amax 448: both quantisations are the
+    # identity, so the fp8a8 linear is the exact product (integer-valued, checked by brute force)
+    rng = np.random.default_rng(22)
+    ints = np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16], np.float64)
+    x = rng.choice(ints, size=(3, 9)) * rng.choice([-1.0, 1.0], size=(3, 9))
+    x[:, 0] = 448.0
+    w = rng.choice(ints, size=(9, 4)) * rng.choice([-1.0, 1.0], size=(9, 4))
+    w[0, :] = 448.0
+    b = np.array([0.5, -1.0, 2.0, 0.0])
+    y = O.dit_linear({"precision": "fp8a8"}, x, w, b)
+    for r in range(3):
+        for o in range(4):
+            assert y[r, o] == sum(x[r, k] * w[k, o] for k in range(9)) + b[o]
+    # bf16 mode leaves the input as it is
+    xr = rng.standard_normal((2, 9))
+    assert np.array_equal(O.dit_linear({"precision": "bf16"}, xr, w, b), O.linear(xr, w, b))

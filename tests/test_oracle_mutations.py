@@ -98,6 +98,13 @@ def _velocity_decode_all_rows(P, cfg, vl, valid, image, s, x, tau, ids):
     return O.action_decoder(P, y[:, 1:, :], ids)
 
 
+def _rows_quantised_per_column(x):
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-2, keepdims=True).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return O.e4m3_decode(O.e4m3_encode((x32 / scale).astype(np.float32))) * scale.astype(np.float64)
+
+
 def _interp_swapped(actions, noise, t):
     t = np.asarray(t, np.float64)[:, None, None]
     return t * np.asarray(noise, np.float64) + (1.0 - t) * np.asarray(actions, np.float64)
@@ -131,6 +138,7 @@ CASES = [
     ("flow_interp", _interp_swapped, pins.test_flow_interp_endpoints),
     ("discretize_t", _bucket_rounded, pins.test_training_bucket_matches_inference_grid),
     ("training_loss", _training_target_sign, pins.test_training_loss_closed_form),
+    ("quantize_e4m3_rows", _rows_quantised_per_column, pins.test_row_quantisation),
 ]
 
 

@@ -807,6 +807,159 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
 }
 
 // ------------------------------------------------------------------------------------
+// W8A8: e4m3 activations x e4m3 weights on the gfx950 fp8 matrix instruction
+// (v_mfma_f32_16x16x128_f8f6f4, both operands e4m3, no block scales). Both operands are
+// byte rows, A [rows][K] (row stride lda bytes) and W [N][K]; one stage holds 128 k of each,
+// i.e. 128-byte rows laid out in LDS as the bf16 kernel's 64-deep tiles (chunk c of row r at
+// position c ^ kswz64(r)), loaded by the same direct-to-LDS ring. A fragment (lane l: row
+// l % 16, k = 32 (l / 16) .. +31, 32 bytes) is two 16-byte LDS reads. Products accumulate in
+// fp32 (k-tiles in order, 128 k per instruction); each accumulator row is then multiplied by
+// its activation scale (a.ascale[row]) and the epilogue applies the weight column scales.
+// ------------------------------------------------------------------------------------
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int BM, int BN, int WM, int WN, int ST, int EK, int GM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_a8_kernel(GemmArgs a, Epi e) {
+  constexpr int BK = 128;            // k (= bytes) of one stage row
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int RPI = 8;             // tile rows per wave load instruction (8 chunks per row)
+  constexpr int A_I = BM / (RPI * NW), B_I = BN / (RPI * NW);
+  static_assert(A_I >= 1 && B_I >= 1 && A_I * RPI * NW == BM && B_I * RPI * NW == BN,
+                "tile rows must split evenly over the waves");
+  static_assert(FM >= 1 && FN >= 1, "tile shape");
+  static_assert(ST >= 2 && ST <= 4, "2 to 4 stages");
+  constexpr int PER_STAGE = A_I + B_I;
+  static_assert(PER_STAGE * (ST - 1) < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * BK], As1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[ST > 2 ? BM * BK : 16], As3[ST > 3 ? BM * BK : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * BK], Bs1[BN * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs2[ST > 2 ? BN * BK : 16], Bs3[ST > 3 ? BN * BK : 16];
+  auto stage_a = [&](auto st) -> uint8_t* {
+    constexpr int V = decltype(st)::value;
+    if constexpr (V == 0) return As0;
+    else if constexpr (V == 1) return As1;
+    else if constexpr (V == 2) return As2;
+    else return As3;
+  };
+  auto stage_b = [&](auto st) -> uint8_t* {
+    constexpr int V = decltype(st)::value;
+    if constexpr (V == 0) return Bs0;
+    else if constexpr (V == 1) return Bs1;
+    else if constexpr (V == 2) return Bs2;
+    else return Bs3;
+  };
+
+  if (a.rows_dev) {
+    a.rows = min(a.rows, *a.rows_dev);
+    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
+  }
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  int tm, tn, split;
+  if (gridDim.z > 1 && gridDim.y == 1 && (8 % gridDim.z) == 0 && ((nm * nn * (int)gridDim.z) & 7) == 0) {
+    split_tile_of<GM>(nm, nn, (int)gridDim.z, tm, tn, split);
+  } else {
+    tile_of<GM>(nm, nn, tm, tn);
+    split = blockIdx.z;
+  }
+  const int r0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * a.k_per_split;
+  const int kend = min(a.K, kbeg + a.k_per_split);
+  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.A, (uint32_t)((long)a.rows * a.lda));
+  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(a.W, (uint32_t)((long)a.N * a.K));
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // load instruction i of this wave fills LDS chunks 64 (wave * X_I + i) .. +63; lane l writes
+  // row l / 8 of that block at chunk position l % 8, which holds k-chunk (l % 8) ^ kswz64(row)
+  int aoff[A_I], akc[A_I], boff[B_I], bkc[B_I];
+#pragma unroll
+  for (int i = 0; i < A_I; ++i) {
+    const int row = (wave * A_I + i) * RPI + (lane >> 3);
+    aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda : OOB;
+    akc[i] = ((lane & 7) ^ kswz64(row & 15)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < B_I; ++i) {
+    const int row = (wave * B_I + i) * RPI + (lane >> 3);
+    boff[i] = (n0 + row < a.N) ? (n0 + row) * a.K : OOB;
+    bkc[i] = ((lane & 7) ^ kswz64(row & 15)) * 16;
+  }
+  // every step issues its loads, also past the last k-tile (out of range: zeros, no traffic)
+  auto issue = [&](auto st, int kt) {
+    uint8_t* sa = stage_a(st);
+    uint8_t* sb = stage_b(st);
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_I; ++i)
+      dma16(ra_rsrc, (uint16_t*)(sa + (wave * A_I + i) * 1024),
+            (k0 + akc[i] < kend && aoff[i] != OOB) ? aoff[i] + k0 + akc[i] : OOB);
+#pragma unroll
+    for (int i = 0; i < B_I; ++i)
+      dma16(rw_rsrc, (uint16_t*)(sb + (wave * B_I + i) * 1024),
+            (k0 + bkc[i] < kend && boff[i] != OOB) ? boff[i] + k0 + bkc[i] : OOB);
+  };
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragment reads: row lane % 16 of the fragment, k-chunks 2 (lane / 16) and 2 (lane / 16) + 1
+  const int fsw = kswz64(lane & 15);
+  const int fp0 = (lane & 15) * BK + (((lane >> 4) * 2) ^ fsw) * 16;
+  const int fp1 = (lane & 15) * BK + (((lane >> 4) * 2 + 1) ^ fsw) * 16;
+  auto frag = [&](const uint8_t* base) -> i32x8_t {
+    const i32x4_t lo = *(const i32x4_t*)(base + fp0);
+    const i32x4_t hi = *(const i32x4_t*)(base + fp1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto compute = [&](auto st) {
+    const uint8_t* sa = stage_a(st);
+    const uint8_t* sb = stage_b(st);
+    i32x8_t af[FM], wf[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = frag(sa + (wm * TM + i * 16) * BK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wf[j] = frag(sb + (wn * TN + j * 16) * BK);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+  auto step = [&](auto st, int kt) {
+    wait_vm_barrier<PER_STAGE * (ST - 2)>();
+    issue(ic<(decltype(st)::value + ST - 1) % ST>{}, kt + ST - 1);
+    compute(st);
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  for_seq<ST - 1>([&](auto i) { issue(i, decltype(i)::value); });
+  int kt = 0;
+  for (; kt + ST <= nk; kt += ST) for_seq<ST>([&](auto i) { step(i, kt + decltype(i)::value); });
+  for_seq<ST - 1>([&](auto i) {
+    if (kt + decltype(i)::value < nk) step(i, kt + decltype(i)::value);
+  });
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // activation row scales (rows past the end keep 1: the epilogue skips them)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = r0 + wm * TM + i * 16 + (lane & 15);
+    const float sr = r < a.rows ? a.ascale[r] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] *= sr;
+  }
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, 0, 0, split, r0, n0, wm, wn, lane, nullptr);
+}
+
+// ------------------------------------------------------------------------------------
 // Skinny MFMA GEMM for <= 64 rows per group (weight streaming: B = 1 projections and
 // the per-embodiment linears). A workgroup owns 16 output columns; its NWAVE waves take
 // contiguous slices of K. Each lane loads its weight fragments (16 B of one weight row)
@@ -1291,6 +1444,43 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     case 3: return mfma_go<32, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
     default: return mfma_go<16, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
   }
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int GM>
+static hipError_t a8_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
+  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
+  dim3 grid(nm * nn, 1, splits);
+  dim3 blk(64 * WM * WN);
+#define GR00T_A8_CASE(K) \
+  case K: hipLaunchKernelGGL((gemm_a8_kernel<BM, BN, WM, WN, ST, K, GM>), grid, blk, 0, s, a, e); break;
+  switch (e.kind) {
+    GR00T_A8_CASE(EPI_STORE)
+    GR00T_A8_CASE(EPI_RESID_ADD)
+    GR00T_A8_CASE(EPI_HEADS)
+    GR00T_A8_CASE(EPI_PARTIAL)
+    default: return hipErrorInvalidValue;
+  }
+#undef GR00T_A8_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_a8(const GemmArgs& a_in, const Epi& e, hipStream_t s) {
+  GemmArgs a = a_in;
+  if (a.rows <= 0 || a.N <= 0) return hipSuccess;
+  if (a.groups != 1 || a.ids != nullptr || a.a_gstride != 0 || a.a_row_off != 0 || a.ln || a.ascale == nullptr)
+    return hipErrorInvalidValue;
+  if (a.K % 16 != 0 || a.lda % 16 != 0 || a.lda < a.K || a.N % 4 != 0) return hipErrorInvalidValue;
+  if ((long)a.rows * a.lda >= (1l << 31) || (long)a.N * a.K >= (1l << 31)) return hipErrorInvalidValue;
+  int splits = 1;
+  if (e.kind == EPI_PARTIAL) {
+    splits = e.splits;
+    if (splits < 1 || a.K % (64 * splits) != 0) return hipErrorInvalidValue;
+  }
+  a.k_per_split = a.K / splits;
+  const int cfg = tile_choice(a.rows, a.N, splits);
+  if (cfg == 0 || cfg == 1) return a8_kind<256, 128, 4, 4, 3, 8>(a, e, splits, s);
+  if (cfg == 5) return a8_kind<128, 64, 4, 2, 4, 16>(a, e, splits, s);
+  return a8_kind<64, 128, 2, 2, 3, 16>(a, e, splits, s);
 }
 
 }  // namespace gr00t

@@ -119,6 +119,8 @@ struct Ws {  // workspace pointers
   uint8_t *code, *bad;
   int *ids, *iota, *vrow, *vcount;
   float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
+  uint8_t* q8;  // W8A8: e4m3 input rows of the current GEMM
+  float* qs;    // W8A8: their row scales
 };
 
 }  // namespace
@@ -204,7 +206,9 @@ int check_config(const gr00t_config* c, std::string& why) {
   if (!(c->act_dtype == GR00T_F32 || c->act_dtype == GR00T_BF16)) return bad("act_dtype must be F32 or BF16");
   if ((c->weight_dtype == GR00T_F32) != (c->act_dtype == GR00T_F32))
     return bad("F32 weights go with F32 activations, BF16/FP8 weights with BF16 activations");
-  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH)) return bad("unknown flag bits");
+  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8)) return bad("unknown flag bits");
+  if ((c->flags & GR00T_FLAG_W8A8) && c->weight_dtype != GR00T_FP8_E4M3)
+    return bad("GR00T_FLAG_W8A8 needs FP8_E4M3 weights");
   return GR00T_OK;
 }
 
@@ -501,7 +505,23 @@ Epi ep_store(void* out, bool f32, long ld, int act = ACT_NONE) {
   return e;
 }
 
+// W8A8: quantise the bf16 input rows to e4m3 (one scale per row), then the fp8 x fp8 GEMM
+hipError_t gemm_a8(gr00t_head* h, const GemmArgs& a_in, const Epi& e, hipStream_t s) {
+  GemmArgs a = a_in;
+  hipError_t r = launch_quant_rows(a.A, a.lda, a.rows, a.K, h->w.q8, a.K, h->w.qs, s, a.rows_dev);
+  if (r != hipSuccess) return r;
+  a.A = h->w.q8;
+  a.lda = a.K;
+  a.ascale = h->w.qs;
+  return launch_gemm_a8(a, e, s);
+}
+
+bool use_a8(const gr00t_head* h, DType at, DType wt) {
+  return (h->cfg.flags & GR00T_FLAG_W8A8) && at == DT_BF16 && wt == DT_FP8;
+}
+
 hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s) {
+  if (use_a8(h, at, wt)) return gemm_a8(h, a, e, s);
   if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 && a.N % 4 == 0)
     return launch_gemm_mfma(a, e, wt, s);
   return launch_gemm_valu(a, e, at, wt, s);
@@ -521,7 +541,7 @@ hipError_t resid_gemm(gr00t_head* h, const GemmArgs& a, DType at, DType wt, long
     e.splits = splits;
     e.split_stride = pstride;
     pend = splits;
-    return launch_gemm_mfma(a, e, wt, s);
+    return use_a8(h, at, wt) ? gemm_a8(h, a, e, s) : launch_gemm_mfma(a, e, wt, s);
   }
   e.kind = EPI_RESID_ADD;
   pend = 0;
@@ -1065,6 +1085,7 @@ int gr00t_finalize(gr00t_head* h) {
   const size_t C = c.num_categories, T = c.time_freq_dim;
   const size_t Sp = round32((int)S), Lmp = round32((int)Lm);
   const size_t ab = act_bytes(h);
+  const bool w8a8 = (c.flags & GR00T_FLAG_W8A8) != 0;
   std::vector<std::pair<void**, size_t>> req = {
       {(void**)&h->w.h, Bm * S * D * 4},      {&h->w.n, Bm * S * D * ab},       {&h->w.q, Bm * S * D * ab},
       {&h->w.k, Bm * Sp * D * ab},            {&h->w.v, Bm * Sp * D * ab},      {&h->w.o, Bm * S * D * ab},
@@ -1078,7 +1099,9 @@ int gr00t_finalize(gr00t_head* h) {
       {(void**)&h->w.iota, C * 4},            {(void**)&h->w.sin_t, K * T * 4},  {(void**)&h->w.t1, K * D * 4},
       {(void**)&h->w.temb, K * D * 4},        {(void**)&h->w.stemb, K * D * 4},
       {(void**)&h->w.ada, K * (Nl + 1) * 2 * D * 4},                              {(void**)&h->w.tauemb, K * D * 4},
-      {(void**)&h->w.c2tab, K * C * D * 4}};
+      {(void**)&h->w.c2tab, K * C * D * 4},
+      {(void**)&h->w.q8, w8a8 ? std::max(Bm * Lm * E, Bm * S * std::max(F, D)) : 0},
+      {(void**)&h->w.qs, w8a8 ? std::max(Bm * Lm, Bm * S) * 4 : 0}};
   size_t total = 0;
   for (auto& r : req) total += (r.second + 255) & ~(size_t)255;
   if (hipMalloc((void**)&h->wsbase, total) != hipSuccess) {

@@ -43,6 +43,7 @@ struct GemmArgs {
   // is given, and rounded to bf16 as the GEMM stages it. One split only.
   int ln;
   const float* ln_ada;
+  const float* ascale;  // W8A8 (launch_gemm_a8): per-row fp32 scales of the e4m3 A rows, NULL otherwise
 };
 
 struct Epi {
@@ -80,6 +81,10 @@ struct Epi {
 
 hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, const Epi& e, DType wt, hipStream_t s);
+// W8A8: e4m3 A rows (a.A, row stride a.lda bytes, row scales a.ascale) times e4m3 weights (a.W,
+// column scales a.wscale) on the gfx950 16x16x128 fp8 MFMA, fp32 accumulation, the epilogue e.
+// Dense (one group), K % 16 == 0, splits as launch_gemm_mfma.
+hipError_t launch_gemm_a8(const GemmArgs& a, const Epi& e, hipStream_t s);
 // Whether a GEMM of `rows` rows and depth K with weights wt can take its A rows through the
 // folded LayerNorm (GemmArgs::ln): at most 32 rows, bf16 weights, 1024 <= K <= 2048, K a
 // multiple of 256, and the staged rows within the kernel's LDS budget.
@@ -152,6 +157,11 @@ hipError_t launch_flow_interp(const float* actions, const float* noise, const fl
 // ones), summed in double in a fixed order (one workgroup); NaN if bad[b] != 0 for some sample.
 hipError_t launch_masked_mse(const float* v_pred, const float* actions, const float* noise, const uint8_t* mask,
                              const uint8_t* bad, int B, int per, float* loss, hipStream_t s);
+// W8A8: bf16 rows x [rows][K] (row stride ldx) -> e4m3 codes q (row stride ldq, bytes) and fp32
+// row scales: scale[r] = amax_r / 448 (1 for an all-zero row), q = e4m3(x / scale) (nearest, ties
+// to even, saturating). Rows >= *rows_dev are skipped when rows_dev is given. K, ldx, ldq % 8 == 0.
+hipError_t launch_quant_rows(const void* x, long ldx, int rows, int K, uint8_t* q, long ldq, float* scale,
+                             hipStream_t s, const int* rows_dev = nullptr);
 // y = SiLU(x), n floats.
 hipError_t launch_silu(const float* x, float* y, long n, hipStream_t s);
 // fp32 -> act dtype copy of n elements.

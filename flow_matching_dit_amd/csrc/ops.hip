@@ -886,6 +886,50 @@ hipError_t launch_masked_mse(const float* v_pred, const float* actions, const fl
   return hipGetLastError();
 }
 
+// W8A8: per-row e4m3 inputs of the e4m3-weight GEMMs ("fp8a8" mode). One wave per row of bf16
+// x: scale[r] = amax_r / 448 (1 for an all-zero row), q[r][k] = e4m3(x[r][k] / scale[r]); both
+// divisions correctly rounded in fp32. Rows r >= *rows_dev (when given) are skipped.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, long ldx, int rows, int K,
+                                                         uint8_t* __restrict__ q, long ldq, float* __restrict__ scale,
+                                                         const int* rows_dev) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows || (rows_dev && row >= *rows_dev)) return;
+  const uint16_t* xr = x + (long)row * ldx;
+  float amax = 0.0f;
+  for (int k = 8 * lane; k < K; k += 512) {  // 8 values (16 bytes) per lane and step
+    const uint4 v = *(const uint4*)(xr + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f(w[i] & 0xFFFFu)), fabsf(bf16_to_f(w[i] >> 16))));
+  }
+  amax = wave_max(amax);
+  const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  if (lane == 0) scale[row] = sc;
+  uint8_t* qr = q + (long)row * ldq;
+  for (int k = 8 * lane; k < K; k += 512) {
+    const uint4 v = *(const uint4*)(xr + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = f_to_e4m3(__fdiv_rn(bf16_to_f(w[i] & 0xFFFFu), sc));
+      const uint32_t hi = f_to_e4m3(__fdiv_rn(bf16_to_f(w[i] >> 16), sc));
+      c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+    }
+    *(uint2*)(qr + k) = make_uint2(c[0], c[1]);
+  }
+}
+
+hipError_t launch_quant_rows(const void* x, long ldx, int rows, int K, uint8_t* q, long ldq, float* scale,
+                             hipStream_t s, const int* rows_dev) {
+  if (rows <= 0) return hipSuccess;
+  if ((K % 8) != 0 || (ldx % 8) != 0 || (ldq % 8) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const uint16_t*)x, ldx, rows, K, q,
+                     ldq, scale, rows_dev);
+  return hipGetLastError();
+}
+
 __global__ void silu_kernel(const float* x, float* y, long n) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = silu_f(x[i]);

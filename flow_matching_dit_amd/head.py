@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libg
 F32, BF16, FP8_E4M3, U8, I32 = 0, 1, 2, 3, 4
 FLAG_STRICT = 0x1
 FLAG_USE_GRAPH = 0x2
+FLAG_W8A8 = 0x4
 
 STATUS = {
     0: "OK", -1: "E_INVALID_ARG", -2: "E_SHAPE", -3: "E_EMBODIMENT", -4: "E_NOT_FINALIZED",
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m flow_matching_dit_amd.build`")
+    # torch (device memory and streams of the callers) ships its own HIP runtime; it is loaded
+    # before the library's, which otherwise initialises the device first and leaves torch's
+    # runtime without a GPU
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     lib.gr00t_create.argtypes = [POINTER(Gr00tConfig), c_int, POINTER(c_void_p)]
     lib.gr00t_create.restype = c_int
@@ -103,7 +108,9 @@ def make_config(cfg, max_batch: int, max_vl_len: int, flags: int = 0, noise_seed
     """Gr00tConfig from a HeadConfig-like object (attributes or dict keys of the same names)."""
     get = (lambda k: cfg[k]) if isinstance(cfg, dict) else (lambda k: getattr(cfg, k))
     prec = get("precision")
-    wdt = {"fp32": F32, "bf16": BF16, "fp8": FP8_E4M3}[prec]
+    wdt = {"fp32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8a8": FP8_E4M3}[prec]
+    if prec == "fp8a8":  # W8A8: e4m3 weights and per-row e4m3 inputs of their GEMMs
+        flags |= FLAG_W8A8
     return Gr00tConfig(get("num_layers"), get("hidden"), get("num_heads"), get("head_dim"), get("ff_dim"),
                        get("vl_dim"), get("state_dim"), get("action_dim"), get("action_horizon"),
                        get("num_categories"), get("num_steps"), get("num_timestep_buckets"),

@@ -58,6 +58,13 @@ typedef enum gr00t_dtype {
 #define GR00T_FLAG_STRICT 0x1u    /* validate ids on the host (one device->host copy) and
                                      refuse unprepared shapes in graph mode */
 #define GR00T_FLAG_USE_GRAPH 0x2u /* replay the K-step loop from a captured hipGraph */
+#define GR00T_FLAG_W8A8 0x4u      /* with FP8_E4M3 weights: the input rows of every e4m3-weight
+                                     GEMM (the DiT's q, k, v, o, MLP and output projections and
+                                     the VL key/value projection) are quantised to e4m3 with one
+                                     fp32 scale per row (amax / 448) and multiplied on the fp8
+                                     matrix cores; FP8 weights required, else GR00T_E_INVALID_ARG
+                                     at create. Adds K + 4 bytes per row of the largest such
+                                     GEMM input to the workspace. */
 
 /*
  * Model and capacity. Widths follow the "Model configuration" table of the

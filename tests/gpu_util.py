@@ -6,7 +6,7 @@ import numpy as np
 from flow_matching_dit_amd import head as H
 from flow_matching_dit_amd import synth
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "fp8a8": 5e-2}
 
 
 def say(*a):

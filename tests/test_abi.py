@@ -71,6 +71,19 @@ def test_create_rejects_mixed_precisions_and_capacity():
     assert lib.gr00t_create(None, 0, ctypes.byref(out)) == -1
 
 
+def test_create_w8a8_flag_needs_fp8_weights():
+    lib = H.load_library()
+    out = ctypes.c_void_p()
+    c = H.make_config(_cfg(precision="bf16"), 1, 8, flags=H.FLAG_W8A8)
+    assert lib.gr00t_create(ctypes.byref(c), 0, ctypes.byref(out)) == -1
+    assert b"W8A8 needs FP8_E4M3" in lib.gr00t_last_error(None)
+    assert out.value is None
+    c = H.make_config(_cfg(precision="fp8a8"), 1, 8)
+    assert c.flags & H.FLAG_W8A8 and c.weight_dtype == H.FP8_E4M3
+    h = H.Gr00tHead(_cfg(precision="fp8a8"), max_batch=2, max_vl_len=8)
+    h.close()
+
+
 def test_load_weights_errors():
     w = synth.WORKLOADS["tiny_fp32_b1"]
     h = H.Gr00tHead(w.cfg, max_batch=1, max_vl_len=32)

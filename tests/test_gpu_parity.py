@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on seeded inputs.
 
 Tolerances (relative L2 of action_pred over every entry, float64):
-fp32 path 1e-4, bf16 2e-2, fp8 e4m3 weights 5e-2.
+fp32 path 1e-4, bf16 2e-2, fp8 e4m3 weights 5e-2, W8A8 (e4m3 weights and per-row e4m3 GEMM
+inputs, against the oracle's W8A8 mode) 5e-2.
 """
 from dataclasses import replace
 
@@ -51,6 +52,7 @@ def test_tiny_fp32_graph_parity():
     ("dit32_bf16_b64", dict(batch=8)),
     ("dit32_bf16_b16_h64", dict(batch=3)),
     ("dit32_fp8_b256", dict(batch=12)),
+    ("dit32_w8a8_b256", dict(batch=12)),
 ])
 def test_small_width_parity(name, kw):
     _parity(small(name, **kw))
@@ -70,6 +72,9 @@ def test_full_width_batch64_two_blocks_parity():
     ("dit32_fp8_b256", 1),    # e4m3 weights, 17 rows: skinny e4m3 kernel
     ("dit32_fp8_b256", 4),    # e4m3 weights, 68 rows: 64 x 128 tiles of weight bytes
     ("dit32_fp8_b256", 64),   # e4m3 weights, 1088 rows: 256 x 128 and 128 x 64 tiles, split-K MLP down
+    ("dit32_w8a8_b256", 1),   # W8A8, 17 rows: 64 x 128 fp8 x fp8 tiles, one ragged row tile
+    ("dit32_w8a8_b256", 4),   # W8A8, 68 rows: 64 x 128 tiles
+    ("dit32_w8a8_b256", 64),  # W8A8, 1088 rows: 256 x 128 and 128 x 64 tiles, split-K MLP down
 ])
 def test_full_width_mid_batch_parity(name, batch):
     # the GEMM configurations between the B=1 and B=64 shapes, at the full width of 1536
@@ -81,6 +86,13 @@ def test_full_width_batch256_bf16_parity():
     # 4352 rows: the MLP up and q,k,v projections take 256 x 256 tiles (GELU and head-major
     # epilogues), the narrow projections 256 x 128; the oracle checks 3 samples
     _parity(small("dit32_bf16_b64", batch=256, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
+            flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 101, 255])
+
+
+def test_full_width_batch256_w8a8_parity():
+    # the W8A8 workload's shapes (4352 rows, 256 x 128 fp8 x fp8 tiles for every DiT GEMM,
+    # 76800 VL rows into the key/value projection) against the oracle's W8A8 mode, 3 samples
+    _parity(small("dit32_w8a8_b256", batch=256, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144),
             flags=H.FLAG_USE_GRAPH, prepare=True, samples=[0, 101, 255])
 
 

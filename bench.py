@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0  # dense e4m3 MFMA (the W8A8 GEMMs)
 METRIC = "action chunks/sec at B=64 and get_action p50 latency (ms) at B=1, 32-layer DiT"
 
 
@@ -41,7 +42,7 @@ def work_per_launch(cls, w, inputs):
     M = B * S
     L = w.vl_len
     Nc = (c.num_layers + 1) // 2
-    wb = 1 if c.precision == "fp8" else 2
+    wb = 1 if c.precision in ("fp8", "fp8a8") else 2  # e4m3 weight bytes
     valid = np.ones((B, L), bool) if inputs["vl_mask"] is None else inputs["vl_mask"].astype(bool)
     nvalid = int(valid.sum())
     if cls in ("qkv_proj", "q_proj", "o_proj", "out_proj", "ff_up", "ff_down"):
@@ -67,7 +68,11 @@ def work_per_launch(cls, w, inputs):
 
 def gpu_leg(args, w, weights, inputs, noise, H, synth):
     import torch
+    from dataclasses import replace
     b1 = synth.WORKLOADS[args.b1_workload]
+    if b1.cfg != w.cfg and b1.cfg.num_layers == w.cfg.num_layers and b1.cfg.hidden == w.cfg.hidden:
+        # the same model in another precision: the B=1 leg takes the handle's configuration
+        b1 = replace(b1, name=f"{b1.name}_{w.cfg.precision}", cfg=w.cfg)
     assert b1.cfg == w.cfg, "the B=1 leg reuses the handle: same model required"
     max_vl = max(w.vl_len, b1.vl_len)
     h = H.Gr00tHead(w.cfg, max_batch=w.batch, max_vl_len=max_vl, flags=H.FLAG_USE_GRAPH)
@@ -167,7 +172,9 @@ def gpu_leg(args, w, weights, inputs, noise, H, synth):
 # Horizon and step-count variants of the same 32-block model (the weights do not depend on
 # either): the base N1.7 horizon of 40 and K in {1, 2, 8, 16} Euler steps.
 VARIANTS = [("dit32_bf16_b1", 40, 4), ("dit32_bf16_b1", 16, 1), ("dit32_bf16_b1", 16, 2),
-            ("dit32_bf16_b1", 16, 8), ("dit32_bf16_b1", 16, 16), ("dit32_bf16_b64", 40, 4)]
+            ("dit32_bf16_b1", 16, 8), ("dit32_bf16_b1", 16, 16), ("dit32_bf16_b64", 40, 4),
+            # B = 256 with e4m3 DiT weights (W8A16) and with per-row e4m3 GEMM inputs (W8A8)
+            ("dit32_fp8_b256", 16, 4), ("dit32_w8a8_b256", 16, 4)]
 
 
 def variants_leg(weights, H, synth, calls=20):
@@ -196,7 +203,8 @@ def variants_leg(weights, H, synth, calls=20):
             ts.append((time.perf_counter() - t) * 1e3)
         h.close()
         p50 = statistics.median(ts)
-        out.append({"workload": w.name, "batch": w.batch, "horizon": hz, "euler_steps": k, "p50_ms": round(p50, 4),
+        out.append({"workload": w.name, "batch": w.batch, "precision": w.cfg.precision, "horizon": hz,
+                    "euler_steps": k, "p50_ms": round(p50, 4),
                     "chunks_per_s": round(w.batch / p50 * 1e3, 1)})
         log(f"[bench] variant {w.name}: p50 {p50:.3f} ms")
     return out
@@ -244,7 +252,9 @@ def roofline(prof, w, inputs, profile_calls, prof_live):
     flops, byts, bound = work_per_launch(best, w, inputs)
     avg_s = ms / n * 1e-3
     if bound == "mfma":
-        achieved, peak, unit = flops / avg_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        # W8A8: the class's e4m3 x e4m3 contraction (its row quantisation inside the timed launch)
+        peak = FP8_PEAK_TFLOPS if w.cfg.precision == "fp8a8" else BF16_PEAK_TFLOPS
+        achieved, unit = flops / avg_s / 1e12, "TFLOP/s"
     else:
         achieved, peak, unit = byts / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
     traffic = None
@@ -276,7 +286,8 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
-                    help="also time the horizon 40 and K = 1, 2, 8, 16 variants (p50 per get_action)")
+                    help="also time the horizon 40 and K = 1, 2, 8, 16 variants and the B = 256 e4m3 and "
+                         "W8A8 configurations (p50 per get_action)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -313,7 +324,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(total_s / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16", "fp32": "f32"}[w.cfg.precision],
+        "scaling": "weak", "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8e4m3-w/bf16", "fp8a8": "fp8e4m3", "fp32": "f32"}[w.cfg.precision],
         "data": "synthetic (seeded N(0,1) VL features/state/noise, N(0,0.02) weights)",
         "config": {"workload": w.name, "batch": w.batch, "vl_len_pad": w.vl_len, "layers": w.cfg.num_layers,
                    "hidden": w.cfg.hidden, "heads": w.cfg.num_heads, "ff": w.cfg.ff_dim,

@@ -1248,6 +1248,22 @@ int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float*
   return GR00T_OK;
 }
 
+int gr00t_quantize_e4m3_rows(gr00t_head* h, const void* x, int64_t ld_x, int32_t rows, int32_t cols, uint8_t* q,
+                             float* scale, void* hip_stream) {
+  if (!h) return GR00T_E_INVALID_ARG;
+  if (!x || !q || !scale) return fail(h, GR00T_E_INVALID_ARG, "gr00t_quantize_e4m3_rows: NULL pointer");
+  if (((uintptr_t)x % 16) || ((uintptr_t)q % 8) || ((uintptr_t)scale % 4))
+    return fail(h, GR00T_E_INVALID_ARG, "gr00t_quantize_e4m3_rows: x must be 16-byte, q 8-byte aligned");
+  if (rows < 0 || cols < 8 || cols % 8 || ld_x < cols || ld_x % 8)
+    return fail(h, GR00T_E_INVALID_ARG,
+                "gr00t_quantize_e4m3_rows: needs rows >= 0, cols a positive multiple of 8, ld_x >= cols and a "
+                "multiple of 8");
+  if (rows == 0) return GR00T_OK;
+  HIPCHK(h, hipSetDevice(h->device));
+  HIPCHK(h, launch_quant_rows(x, ld_x, rows, cols, q, cols, scale, (hipStream_t)hip_stream));
+  return GR00T_OK;
+}
+
 void gr00t_destroy(gr00t_head* h) {
   if (!h) return;
   if (h->finalized || h->arena || h->wsbase) (void)hipSetDevice(h->device);

@@ -29,7 +29,8 @@ STATUS = {
 
 # Every exported symbol of include/gr00t_head.h.
 EXPORTS = ("gr00t_create", "gr00t_load_weights", "gr00t_finalize", "gr00t_prepare", "gr00t_get_action",
-           "gr00t_get_action_reuse_vl", "gr00t_train_forward", "gr00t_velocity", "gr00t_destroy",
+           "gr00t_get_action_reuse_vl", "gr00t_train_forward", "gr00t_velocity", "gr00t_quantize_e4m3_rows",
+           "gr00t_destroy",
            "gr00t_last_error", "gr00t_device_bytes", "gr00t_profile_enable", "gr00t_profile_read",
            "gr00t_profile_class_name")
 
@@ -88,6 +89,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gr00t_train_forward.restype = c_int
     lib.gr00t_velocity.argtypes = [c_void_p, POINTER(Gr00tInputs), c_int32, c_void_p, c_void_p]
     lib.gr00t_velocity.restype = c_int
+    lib.gr00t_quantize_e4m3_rows.argtypes = [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
+                                             c_void_p]
+    lib.gr00t_quantize_e4m3_rows.restype = c_int
     lib.gr00t_destroy.argtypes = [c_void_p]
     lib.gr00t_destroy.restype = None
     lib.gr00t_last_error.argtypes = [c_void_p]
@@ -230,6 +234,19 @@ class Gr00tHead:
         self._check(self.lib.gr00t_velocity(self.h, ctypes.byref(inp), step_k, c_void_p(out.data_ptr()),
                                             self._stream(stream)))
         return out
+
+    def quantize_e4m3_rows(self, x, stream=None):
+        """Per-row e4m3 codes [rows, cols] uint8 and fp32 scales [rows] of a bf16 device matrix
+        [rows, cols] (the W8A8 mode's quantisation of a GEMM input)."""
+        import torch
+        if x.dtype != torch.bfloat16 or x.dim() != 2:
+            raise ValueError("x must be a 2-D bfloat16 tensor")
+        rows, cols = int(x.shape[0]), int(x.shape[1])
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+        self._check(self.lib.gr00t_quantize_e4m3_rows(self.h, _ptr(x), cols, rows, cols, c_void_p(q.data_ptr()),
+                                                      c_void_p(scale.data_ptr()), self._stream(stream)))
+        return q, scale
 
     def profile(self, on=True):
         """on: False/0 off, True/1 every launch (eager), 2 graph kept (launches outside it timed)."""

@@ -209,6 +209,21 @@ int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* acti
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v,
                    void* hip_stream);
 
+/*
+ * The per-row e4m3 quantisation of the W8A8 mode (GR00T_FLAG_W8A8), as its GEMMs apply it
+ * to their inputs; the fp8 format is the OCP e4m3fn of the architecture page's fp8 weights
+ * (max 448). x: [rows][ld_x] bf16, device, 16-byte aligned; q: [rows][cols] e4m3 codes,
+ * device, 8-byte aligned; scale: [rows] f32, device. For each row r:
+ * scale[r] = fp32(max_k |x[r][k]|) / 448 (1 for an all-zero row) and q[r][k] = the e4m3
+ * code nearest to the fp32 quotient x[r][k] / scale[r] (ties to the even code, magnitudes
+ * above 448 saturate, the sign bit follows the quotient's sign), both divisions correctly
+ * rounded in fp32. Needs a created handle (for its device and error message); enqueued on
+ * `hip_stream`. E_INVALID_ARG for NULL pointers, misaligned x or q, rows < 0, cols not a
+ * positive multiple of 8, or ld_x < cols / not a multiple of 8; rows == 0 does nothing.
+ */
+int gr00t_quantize_e4m3_rows(gr00t_head* h, const void* x, int64_t ld_x, int32_t rows, int32_t cols,
+                             uint8_t* q, float* scale, void* hip_stream);
+
 /* Release graphs, device weights and workspace. NULL is a no-op. */
 void gr00t_destroy(gr00t_head* h);
 

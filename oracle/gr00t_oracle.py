@@ -124,11 +124,17 @@ def quantize_e4m3_rows(x) -> np.ndarray:
     e4m3 weights. scale[r] = fp32(max_k |x[r,k]|) / fp32(448) (fp32 division; 1 for an all-zero
     row), code = e4m3(fp32(x / scale)) decided on fp32 operands, dequantised x = decode(code) *
     scale: the column quantisation of the weights applied along the rows."""
+    codes, scale = quantize_e4m3_rows_codes(x)
+    return e4m3_decode(codes) * scale.astype(np.float64)[..., None]
+
+
+def quantize_e4m3_rows_codes(x):
+    """The codes [.., rows, cols] (uint8) and fp32 scales [.., rows] of quantize_e4m3_rows."""
     x32 = np.ascontiguousarray(x, dtype=np.float32)
     amax = np.max(np.abs(x32), axis=-1, keepdims=True).astype(np.float32)
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     codes = e4m3_encode((x32 / scale).astype(np.float32))
-    return e4m3_decode(codes) * scale.astype(np.float64)
+    return codes, scale[..., 0]
 
 
 # --------------------------------------------------------------------------

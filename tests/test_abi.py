@@ -22,7 +22,7 @@ def _cfg(**kw):
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "gr00t_head.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gr00t_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gr00t_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -176,6 +176,24 @@ def test_train_forward_validates_before_device_work():
     assert lib.gr00t_train_forward(h.h, ctypes.byref(inp), None, t, loss, None, None) == -4  # not finalized first
     assert lib.gr00t_train_forward(h.h, ctypes.byref(_fake_inputs(3, 8)), act, t, loss, None, None) == -2
     assert lib.gr00t_train_forward(None, ctypes.byref(inp), act, t, loss, None, None) == -1
+    h.close()
+
+
+def test_quantize_validates_before_device_work():
+    lib = H.load_library()
+    h = H.Gr00tHead(synth.TINY, max_batch=1, max_vl_len=8)
+    x, q, sc = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    cases = [((None, 16, 2, 16, q, sc), b"NULL"), ((x, 16, 2, 16, q, None), b"NULL"),
+             ((ctypes.c_void_p(0x1008), 16, 2, 16, q, sc), b"aligned"),
+             ((x, 16, 2, 16, ctypes.c_void_p(0x2004), sc), b"aligned"),
+             ((x, 16, -1, 16, q, sc), b"rows >= 0"), ((x, 16, 2, 12, q, sc), b"multiple of 8"),
+             ((x, 16, 2, 0, q, sc), b"multiple of 8"), ((x, 8, 2, 16, q, sc), b"ld_x"),
+             ((x, 20, 2, 16, q, sc), b"ld_x")]
+    for args, msg in cases:
+        assert lib.gr00t_quantize_e4m3_rows(h.h, *args, None) == -1
+        assert msg in lib.gr00t_last_error(h.h)
+    assert lib.gr00t_quantize_e4m3_rows(h.h, x, 16, 0, 16, q, sc, None) == 0  # no rows: no device work
+    assert lib.gr00t_quantize_e4m3_rows(None, x, 16, 1, 16, q, sc, None) == -1
     h.close()
 
 

@@ -19,6 +19,7 @@ CASES = [
     ("dit32_bf16_b64", [0, 17, 63]),
     ("dit32_bf16_b16_h64", [6]),
     ("dit32_fp8_b256", [0, 200, 255]),
+    ("dit32_w8a8_b256", [0, 128, 255]),
 ]
 
 

@@ -36,6 +36,7 @@ def _gpu_train(h, inp, noise, actions, t):
     ("dit32_bf16_b1", dict(batch=3)),                                             # image / text split
     ("dit32_bf16_b64", dict(batch=8)),                                            # ragged VL, action mask
     ("dit32_bf16_b64", dict(batch=8, num_layers=2, hidden=1536, num_heads=32, ff_dim=6144)),  # full width
+    ("dit32_w8a8_b256", dict(batch=8)),                                           # W8A8 GEMMs
 ])
 def test_train_forward_matches_oracle(name, kw):
     w = synth.WORKLOADS[name] if kw is None else small(name, **kw)

@@ -23,11 +23,13 @@ def _other(inputs, noise, seed):
     return inp, rng.standard_normal(noise.shape).astype(np.float32)
 
 
-@pytest.mark.parametrize("graph", [False, True], ids=["eager", "graph"])
-def test_reuse_vl_equals_full_call(graph):
+@pytest.mark.parametrize("name,graph", [("dit32_bf16_b1", False), ("dit32_bf16_b1", True), ("dit32_w8a8_b256", True)],
+                         ids=["eager", "graph", "w8a8-graph"])
+def test_reuse_vl_equals_full_call(name, graph):
     import torch
-    # 3 samples with the image/text split: text blocks and image blocks use different key masks
-    w = small("dit32_bf16_b1", batch=3)
+    # 3 samples (the bf16 case with the image/text split: text blocks and image blocks use
+    # different key masks); W8A8: the cached keys and values come from e4m3 VL rows
+    w = small(name, batch=3)
     say(f"[vl-cache] {w.name} B={w.batch} L={w.vl_len} graph={graph}")
     wt, inp, nz = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
     flags = H.FLAG_USE_GRAPH if graph else 0

@@ -458,6 +458,10 @@ def test_row_quantisation():
         # every value is its row's scale times an e4m3 value
         assert np.all(np.isin(np.abs(q[r]) / np.float64(scale), O._E4M3_POS))
     assert np.array_equal(O.quantize_e4m3_rows(np.zeros((2, 5))), np.zeros((2, 5)))
+    codes, scales = O.quantize_e4m3_rows_codes(x)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32 and scales.shape == (4,)
+    assert np.array_equal(O.e4m3_decode(codes) * scales[:, None].astype(np.float64), q)
+    assert np.all(np.max(codes & 0x7F, axis=1) == 0x7E)  # each row's amax element encodes 448
     # rows whose amax is 448 (scale 1) of e4m3-representable values are unchanged
     v = O._E4M3_POS[rng.integers(0, 127, size=(3, 30))] * rng.choice([-1.0, 1.0], size=(3, 30))
     v[:, 0] = 448.0

@@ -43,28 +43,6 @@ __device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
 
 __device__ __forceinline__ float e4m3_to_f(uint32_t c) { return bf16_to_f(e4m3_to_bf16(c)); }
 
-// fp32 -> OCP e4m3 code: nearest value, ties to the even code, magnitudes above 448 saturate
-// to 448 (0x7E); the sign bit follows the sign of v (also for -0). Finite inputs.
-__device__ __forceinline__ uint32_t f_to_e4m3(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float f = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (f < 0.015625f) {  // below the smallest normal 2^-6: multiples of 2^-9 (8 * 2^-9 = 2^-6 is code 0x08)
-    code = (uint32_t)rintf(f * 512.0f);
-  } else {
-    const uint32_t b = __float_as_uint(f);
-    uint32_t ex = (b >> 23) - 120u;  // biased e4m3 exponent, 1 .. 15
-    const uint32_t keep = (b >> 20) & 7u, rest = b & 0xFFFFFu;
-    uint32_t m = keep + ((rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u);
-    if (m == 8u) {
-      m = 0u;
-      ex += 1u;
-    }
-    code = min((ex << 3) | m, 0x7Eu);
-  }
-  return code | sign;
-}
-
 template <typename T>
 __device__ __forceinline__ float ld(const T* p);
 template <>

@@ -888,7 +888,10 @@ hipError_t launch_masked_mse(const float* v_pred, const float* actions, const fl
 
 // W8A8: per-row e4m3 inputs of the e4m3-weight GEMMs ("fp8a8" mode). One wave per row of bf16
 // x: scale[r] = amax_r / 448 (1 for an all-zero row), q[r][k] = e4m3(x[r][k] / scale[r]); both
-// divisions correctly rounded in fp32. Rows r >= *rows_dev (when given) are skipped.
+// divisions correctly rounded in fp32. The codes come from the gfx950 conversion instruction
+// (v_cvt_pk_fp8_f32, round to nearest even): it equals the nearest-even OCP e4m3 code, sign
+// included, on every fp32 value of magnitude up to 460 (checked exhaustively on the GPU), and the
+// quotients stay below 448 * (1 + 2^-23). Rows r >= *rows_dev (when given) are skipped.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, long ldx, int rows, int K,
                                                          uint8_t* __restrict__ q, long ldq, float* __restrict__ scale,
                                                          const int* rows_dev) {
@@ -910,14 +913,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   for (int k = 8 * lane; k < K; k += 512) {
     const uint4 v = *(const uint4*)(xr + k);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t c[2] = {0u, 0u};
+    float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f_to_e4m3(__fdiv_rn(bf16_to_f(w[i] & 0xFFFFu), sc));
-      const uint32_t hi = f_to_e4m3(__fdiv_rn(bf16_to_f(w[i] >> 16), sc));
-      c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+      f[2 * i] = __fdiv_rn(bf16_to_f(w[i] & 0xFFFFu), sc);
+      f[2 * i + 1] = __fdiv_rn(bf16_to_f(w[i] >> 16), sc);
     }
-    *(uint2*)(qr + k) = make_uint2(c[0], c[1]);
+    int c0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    c0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], c0, true);
+    int c1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    c1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], c1, true);
+    *(uint2*)(qr + k) = make_uint2((uint32_t)c0, (uint32_t)c1);
   }
 }
 

@@ -58,6 +58,15 @@ def test_small_width_parity(name, kw):
     _parity(small(name, **kw))
 
 
+@pytest.mark.parametrize("precision", ["fp8", "fp8a8"])
+def test_ragged_vl_fp8_modes_parity(precision):
+    # the B=64 recipe (ragged VL lengths, action mask) with e4m3 weights, and with W8A8: the
+    # key/value projection then runs over the compacted valid rows only (device row count)
+    w = small("dit32_bf16_b64", batch=8)
+    w = replace(w, name=f"{w.name}_{precision}", cfg=replace(w.cfg, precision=precision))
+    _parity(w, flags=H.FLAG_USE_GRAPH, prepare=True)
+
+
 def test_full_width_batch64_two_blocks_parity():
     # 64 samples of 17 tokens at width 1536: every block GEMM runs at its full-size shape
     # (1088 rows; the MLP down projection in 4 K-splits); the oracle checks 3 samples

@@ -4,10 +4,11 @@
 //    (v_mfma_f32_16x16x32_bf16), fp32 accumulation. Tiles of A [BM x 64] and
 //    W [BN x 64] go from memory straight into LDS (buffer_load ... lds) through a
 //    ring of 3 stages, so two tiles of loads are in flight while one is multiplied.
-//  * gemm_mfma_kernel: the same product for e4m3 weights (and the small tiles).
-//    Tiles go global -> registers -> LDS (double buffered); e4m3 weights are decoded
-//    to bf16 (exactly) on their way into LDS and the per-column scale is applied in
-//    the epilogue.
+//    e4m3 weights take the same kernel with their bytes in LDS, each fragment decoded
+//    to bf16 (exactly) after its LDS read; the per-column scale is applied in the
+//    epilogue.
+//  * gemm_a8_kernel: e4m3 activations x e4m3 weights (W8A8) on the fp8 matrix
+//    instruction (v_mfma_f32_16x16x128_f8f6f4), with per-row and per-column scales.
 //    Both load through buffer descriptors, so rows or k beyond the matrix read as
 //    zero without branches.
 //    The MFMA computes C^T = W A^T per 16x16 fragment, so every lane ends with four
@@ -358,180 +359,6 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, bool FP8, int EK, int PF = 1, int WPE = 1, int PAD = 8, int GM = 16>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE))) void gemm_mfma_kernel(GemmArgs a,
-                                                                                                            Epi e) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 fragment");
-  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-  constexpr int MF_BK = BK;
-  constexpr int MF_LDS_LD = BK + PAD;              // bf16 per LDS row (padding staggers rows across banks)
-  constexpr int CPR = BK / 8;                      // 16-byte bf16 chunks per row
-  constexpr int CPR8 = BK / 16;                    // 16-byte e4m3 chunks per row
-  constexpr int A_CHUNKS = BM * CPR;
-  constexpr int B_CHUNKS = FP8 ? BN * CPR8 : BN * CPR;
-  constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
-  constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * MF_LDS_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * MF_LDS_LD];
-
-  if (a.rows_dev) {  // row count known on the device only: the grid covers the maximum,
-    // the tiles of the actual rows are dealt over all workgroup ids (and so all XCDs)
-    a.rows = min(a.rows, *a.rows_dev);
-    if ((int)blockIdx.x >= ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN)) return;
-  }
-  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of<GM>(nm, nn, tm, tn);
-  const int g = blockIdx.y;
-  const int split = blockIdx.z;
-  const int cat = a.ids ? a.ids[g] : 0;
-  const int r0 = tm * BM, n0 = tn * BN;
-  const int kper = a.k_per_split;
-  const int kbeg = split * kper;
-  const int kend = min(a.K, kbeg + kper);
-
-  const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
-  const uint32_t wes = FP8 ? 1 : 2;
-  const char* Wb = (const char*)a.W + (long)cat * a.w_cstride * wes;
-  // Descriptors cover exactly the valid rows of this group: everything past them reads 0.
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
-  const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(Wb, (uint32_t)((long)a.N * a.K * wes));
-
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // Per-thread global byte offsets of its chunks at k = 0 (OOB for chunks past the tile).
-  int aoff[A_PER], boff[B_PER];
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int c = t + i * NT;
-    const int row = c / CPR, kc = (c % CPR) * 8;
-    aoff[i] = (c < A_CHUNKS && r0 + row < a.rows) ? ((r0 + row) * (int)a.lda + kc) * 2 : OOB;
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int c = t + i * NT;
-    if (FP8) {
-      const int n = c / CPR8, kc = (c % CPR8) * 16;
-      boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) : OOB;
-    } else {
-      const int n = c / CPR, kc = (c % CPR) * 8;
-      boff[i] = (c < B_CHUNKS && n0 + n < a.N) ? ((n0 + n) * a.K + kc) * 2 : OOB;
-    }
-  }
-
-  // Two register sets of global loads alternate, so every tile's loads are issued two
-  // tiles of MFMAs before they are written to LDS.
-  uint4 ra0[A_PER], rb0[B_PER];
-  uint4 ra1[PF == 2 ? A_PER : 1], rb1[PF == 2 ? B_PER : 1];
-  auto gload = [&](auto& ra, auto& rb, int k0) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int kc = ((t + i * NT) % CPR) * 8;
-      const bool in = aoff[i] != OOB && k0 + kc < kend;
-      ra[i] = buf_load16(ra_rsrc, in ? aoff[i] + k0 * 2 : OOB);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int kc = FP8 ? ((t + i * NT) % CPR8) * 16 : ((t + i * NT) % CPR) * 8;
-      const bool in = boff[i] != OOB && k0 + kc < kend;
-      rb[i] = buf_load16(rw_rsrc, in ? boff[i] + k0 * (int)wes : OOB);
-    }
-  };
-  auto lstore = [&](const auto& ra, const auto& rb, int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = t + i * NT;
-      if ((A_CHUNKS % NT) == 0 || c < A_CHUNKS) *(uint4*)&As[buf][(c / CPR) * MF_LDS_LD + (c % CPR) * 8] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = t + i * NT;
-      if ((B_CHUNKS % NT) == 0 || c < B_CHUNKS) {
-        if (FP8) {
-          const int n = c / CPR8, kc = (c % CPR8) * 16;
-          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc] = make_uint4(e4m3x2_to_bf16x2(rb[i].x), e4m3x2_to_bf16x2(rb[i].x >> 16),
-                                                             e4m3x2_to_bf16x2(rb[i].y), e4m3x2_to_bf16x2(rb[i].y >> 16));
-          *(uint4*)&Bs[buf][n * MF_LDS_LD + kc + 8] = make_uint4(e4m3x2_to_bf16x2(rb[i].z), e4m3x2_to_bf16x2(rb[i].z >> 16),
-                                                                 e4m3x2_to_bf16x2(rb[i].w), e4m3x2_to_bf16x2(rb[i].w >> 16));
-        } else {
-          *(uint4*)&Bs[buf][(c / CPR) * MF_LDS_LD + (c % CPR) * 8] = rb[i];
-        }
-      }
-    }
-  };
-
-  floatx4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t af[FM], wf[FN];
-      const int koff = ks * 32 + (lane >> 4) * 8;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8_t*)&As[buf][(wm * TM + i * 16 + (lane & 15)) * MF_LDS_LD + koff];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        wf[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN + j * 16 + (lane & 15)) * MF_LDS_LD + koff];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int nk = (kend - kbeg + MF_BK - 1) / MF_BK;
-  if (PF == 1) {
-    // one register set: tile kt + 1 is loaded while tile kt is multiplied
-    if (nk > 0) {
-      gload(ra0, rb0, kbeg);
-      lstore(ra0, rb0, 0);
-      __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload(ra0, rb0, kbeg + (kt + 1) * MF_BK);
-      compute(buf);
-      if (kt + 1 < nk) lstore(ra0, rb0, buf ^ 1);
-      __syncthreads();
-    }
-  } else {
-    // two register sets: tile T lives in LDS buffer T & 1, set 0 carries even tiles and
-    // set 1 odd tiles, so every load is issued two tiles of MFMAs before its LDS store
-    if (nk > 0) {
-      gload(ra0, rb0, kbeg);
-      if (nk > 1) gload(ra1, rb1, kbeg + MF_BK);
-      lstore(ra0, rb0, 0);
-      __syncthreads();
-      if (nk > 2) gload(ra0, rb0, kbeg + 2 * MF_BK);
-    }
-    for (int kt = 0; kt < nk; kt += 2) {
-      compute(0);                            // tile kt
-      if (kt + 1 < nk) lstore(ra1, rb1, 1);  // tile kt + 1
-      __syncthreads();
-      if (kt + 3 < nk) gload(ra1, rb1, kbeg + (kt + 3) * MF_BK);
-      if (kt + 1 >= nk) break;
-      compute(1);                            // tile kt + 1
-      if (kt + 2 < nk) lstore(ra0, rb0, 0);  // tile kt + 2
-      __syncthreads();
-      if (kt + 4 < nk) gload(ra0, rb0, kbeg + (kt + 4) * MF_BK);
-    }
-  }
-
-  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane);
-}
-
 // ------------------------------------------------------------------------------------
 // bf16 x bf16 MFMA GEMM whose tiles go straight from memory into LDS
 // (buffer_load_dwordx4 ... lds, gfx950), through a ring of ST stages: the loads of
@@ -545,7 +372,7 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
 //    chunk h = (row / 8) + 2 * c of either row sits at position h ^ L of the line.
 // Both keep every fragment read free of LDS bank conflicts (the plain row-major XOR for
 // 64-byte rows measured half of all LDS cycles as conflicts).
-// The accumulation order (k-tiles in order, 32 k per MFMA) is that of gemm_mfma_kernel.
+// Accumulation order: k-tiles in order, 32 k per MFMA.
 // ------------------------------------------------------------------------------------
 // Waits until at most N vector-memory operations of this wave are in flight and all its
 // LDS reads have completed, then meets the workgroup barrier. One asm statement, so the
@@ -1294,38 +1121,12 @@ hipError_t launch_gemm_valu(const GemmArgs& a, const Epi& e, DType at, DType wt,
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, bool FP8, int PAD, int GM>
-static hipError_t mfma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
-  const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
-  dim3 grid(nm * nn, a.groups, splits);
-  dim3 blk(64 * WM * WN);
-#define GR00T_MFMA_CASE(K) \
-  case K: hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, BK, FP8, K, 1, 1, PAD, GM>), grid, blk, 0, s, a, e); break;
-  switch (e.kind) {
-    GR00T_MFMA_CASE(EPI_STORE)
-    GR00T_MFMA_CASE(EPI_RESID_ADD)
-    GR00T_MFMA_CASE(EPI_HEADS)
-    GR00T_MFMA_CASE(EPI_EULER)
-    GR00T_MFMA_CASE(EPI_PARTIAL)
-    default: return hipErrorInvalidValue;
-  }
-#undef GR00T_MFMA_CASE
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int BK, int PAD, int GM>
-static hipError_t mfma_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
-  return fp8 ? mfma_kind<BM, BN, WM, WN, BK, true, PAD, GM>(a, e, splits, s)
-             : mfma_kind<BM, BN, WM, WN, BK, false, PAD, GM>(a, e, splits, s);
-}
-
-// Tile configurations (measured on the head's shapes; LDS rows padded by 16 bf16, which
-// removes LDS bank conflicts for 64-deep tiles):
-//   0: 256x128, 8 waves, BK 32, raster group 4   (many tiles: VL K/V projection, B >= 256)
-//   1: 256x128, 8 waves, BK 64, raster group 8   (B ~ 64: MLP up, fused qkv)
-//   2: 64x128, 4 waves, BK 64                    (fewer tiles: D-wide outputs, split-K)
-//   3: 32x64, 4 waves                            (<= 32 rows)
-//   4: 16x64, 4 waves                            (<= 16 rows)
+// Tile configurations of the matrix-core GEMMs (tile_choice; measured on the head's shapes):
+//   0: 256 x 256 (bf16; e4m3 weights 256 x 128), 16 waves   (many tiles: VL K/V projection, B >= 256)
+//   1: 256 x 128, 16 waves, 64 k per stage, 3 stages        (B ~ 64: MLP up and down, fused q,k,v)
+//   2: 64 x 128, 4 waves                                    (few tiles)
+//   5: 128 x 64, 8 waves, 4 stages                          (narrow outputs: q and o projections)
+// (3 and 4 name the <= 32 and <= 16 row cases, which the skinny kernels serve.)
 template <int BM, int BN, int WM, int WN, int BK, int ST, int GM, bool W8 = false>
 static hipError_t dma_kind(const GemmArgs& a, const Epi& e, int splits, hipStream_t s) {
   const int nm = (a.rows + BM - 1) / BM, nn = (a.N + BN - 1) / BN;
@@ -1437,13 +1238,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     if (cfg == 2) return dma_kind<64, 128, 2, 2, 64, 3, 16, true>(a, e, splits, s);
     if (cfg == 5) return dma_kind<128, 64, 4, 2, 64, 4, 16, true>(a, e, splits, s);
   }
-  switch (cfg == 5 ? 2 : cfg) {  // e4m3 weights: 64 x 128 tiles for narrow outputs too
-    case 0: return mfma_go<256, 128, 4, 2, 32, 16, 4>(a, e, fp8, splits, s);
-    case 1: return mfma_go<256, 128, 4, 2, 64, 16, 8>(a, e, fp8, splits, s);
-    case 2: return mfma_go<64, 128, 2, 2, 64, 16, 16>(a, e, fp8, splits, s);
-    case 3: return mfma_go<32, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
-    default: return mfma_go<16, 64, 1, 4, 64, 16, 16>(a, e, fp8, splits, s);
-  }
+  return hipErrorInvalidValue;  // more than 64 rows always selects one of the tiles above
 }
 
 template <int BM, int BN, int WM, int WN, int ST, int GM>

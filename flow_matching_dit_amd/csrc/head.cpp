@@ -520,6 +520,15 @@ bool use_a8(const gr00t_head* h, DType at, DType wt) {
   return (h->cfg.flags & GR00T_FLAG_W8A8) && at == DT_BF16 && wt == DT_FP8;
 }
 
+// W8A8 GEMM whose input rows a LayerNorm has already written as e4m3 codes and row scales
+hipError_t gemm_q8(gr00t_head* h, const GemmArgs& a_in, const Epi& e, hipStream_t s) {
+  GemmArgs a = a_in;
+  a.A = h->w.q8;
+  a.lda = a.K;
+  a.ascale = h->w.qs;
+  return launch_gemm_a8(a, e, s);
+}
+
 hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s) {
   if (use_a8(h, at, wt)) return gemm_a8(h, a, e, s);
   if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 && a.N % 4 == 0)
@@ -813,6 +822,11 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     // skinny kernel normalises the fp32 rows of h as it stages them) and the o projection
     // adds into h directly: one launch fewer per block.
     const bool fold = A == DT_BF16 && dw == DT_BF16 && gemm_ln_fits((int)M, D, dw);
+    // W8A8: the LayerNorms before the q / q,k,v, MLP-up and output projections write e4m3 rows
+    const bool a8 = use_a8(h, A, dw);
+    void* ny = a8 ? (void*)h->w.q8 : h->w.n;
+    const DType nt = a8 ? DT_FP8 : A;
+    float* nq = a8 ? h->w.qs : nullptr;
     auto normed = [&](int N, const float* ada) {  // A operand of a GEMM that reads LN(h)
       GemmArgs a = ga(fold ? (const void*)h->w.h : (const void*)h->w.n, D, (int)M, N, D);
       if (fold) {
@@ -826,8 +840,8 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     for (int l = 0; l < Nl; ++l) {
       const LayerOff& lo = lay.L[l];
       const bool self = (l % 2) == 1;
-      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada_of(l), s,
-                                                   ada_rows, ada_stride));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, ny, nt, (int)M, D, ada_of(l), s,
+                                                   ada_rows, ada_stride, nq));
       pend = 0;
       {
         GemmArgs a = ga(h->w.n, D, (int)M, (self ? 3 : 1) * D, D);
@@ -848,7 +862,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         e.pstride[0] = S;
         e.pstride[1] = e.pstride[2] = Sp;
         e.transposed[2] = 1;
-        LAUNCH(h, s, self ? K_QKV_PROJ : K_Q_PROJ, gemm(h, a, e, A, dw, s));
+        LAUNCH(h, s, self ? K_QKV_PROJ : K_Q_PROJ, a8 ? gemm_q8(h, a, e, s) : gemm(h, a, e, A, dw, s));
       }
       AttnArgs at_{};
       at_.q = h->w.q;
@@ -881,14 +895,16 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.so) : nullptr;
         LAUNCH(h, s, K_O_PROJ, resid_gemm(h, a, A, dw, pstride, pend, s, fold));
       }
-      if (!fold) LAUNCH(h, s, K_NORM3, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, nullptr, s));
+      if (!fold)
+        LAUNCH(h, s, K_NORM3, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, ny, nt, (int)M, D, nullptr, s, 0, 0, nq));
       pend = 0;
       {
         GemmArgs a = normed(F, nullptr);
         a.W = at<void>(h, lo.w1);
         a.bias = at<float>(h, lo.b1);
         a.wscale = dw == DT_FP8 ? at<float>(h, lo.s1) : nullptr;
-        LAUNCH(h, s, K_FF_UP, gemm(h, a, ep_store(h->w.u, f32, F, ACT_GELU), A, dw, s));
+        const Epi eu = ep_store(h->w.u, f32, F, ACT_GELU);
+        LAUNCH(h, s, K_FF_UP, a8 ? gemm_q8(h, a, eu, s) : gemm(h, a, eu, A, dw, s));
         a = ga(h->w.u, F, (int)M, D, F);
         a.W = at<void>(h, lo.w2);
         a.bias = at<float>(h, lo.b2);
@@ -898,13 +914,14 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     }
     // ---- output adaLN + projection, then decoder and Euler update
     {
-      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, h->w.n, A, (int)M, D, ada_of(Nl), s,
-                                                   ada_rows, ada_stride));
+      LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, ny, nt, (int)M, D, ada_of(Nl), s,
+                                                   ada_rows, ada_stride, nq));
       GemmArgs a = ga(h->w.n, D, (int)M, D, D);
       a.W = at<void>(h, lay.p_w);
       a.bias = at<float>(h, lay.p_b);
       a.wscale = dw == DT_FP8 ? at<float>(h, lay.p_s) : nullptr;
-      LAUNCH(h, s, K_OUT_PROJ, gemm(h, a, ep_store(h->w.y, f32, D), A, dw, s));
+      const Epi ey = ep_store(h->w.y, f32, D);
+      LAUNCH(h, s, K_OUT_PROJ, a8 ? gemm_q8(h, a, ey, s) : gemm(h, a, ey, A, dw, s));
       a = ga(h->w.y, D, H, D, D);
       a.groups = B;
       a.a_gstride = S;

@@ -108,9 +108,11 @@ hipError_t launch_compact_rows(const uint8_t* code, int n, int* idx, int* count,
 // partials may be NULL (nsplit = 0): then it is launch_layernorm on fp32 h.
 // ada_rows > 0: row r takes its modulation from ada + (r / ada_rows) * ada_stride (one
 // [scale | shift] per sample of ada_rows rows); 0: every row uses ada.
+// yt = DT_FP8 (W8A8): y receives the e4m3 codes [rows][D] of the bf16-rounded output and
+// qscale[rows] their row scales, as launch_quant_rows would make them from a bf16 y.
 hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y,
                                   DType yt, int rows, int D, const float* ada, hipStream_t s, int ada_rows = 0,
-                                  long ada_stride = 0);
+                                  long ada_stride = 0, float* qscale = nullptr);
 
 // Multi-head attention per (sample, head): softmax(q k^T / sqrt(hd)) v.
 // q [B][nh][S][hd]; k [B][nh][Lp][hd] (keys row-major, Lp = Lk rounded up to 32);

@@ -81,11 +81,15 @@ hipError_t launch_layernorm(const void* x, DType xt, long ldx, void* y, DType yt
 // Residual add of split-K partial sums fused with the next (ada)LayerNorm: one wave per
 // row, float4 accesses (lane owns columns 4*lane + 256*i .. +3); the row of h is updated
 // in place (h + p_0 + p_1 + ..., fixed order) and normalised. D % 4 == 0, D <= 2048.
+// TY = uint8_t (W8A8): the normalised row is rounded to bf16 as for a bf16 output, then
+// written as the e4m3 codes of quant_rows_kernel (row scale amax / 448 into qscale[row],
+// codes of the correctly rounded quotients), so the GEMM reads it without a separate pass.
 template <typename TY, int NS>
 __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict__ h, const float* __restrict__ part,
                                                               long split_stride, TY* __restrict__ y, int rows, int D,
                                                               const float* __restrict__ ada_base, int ada_rows,
-                                                              long ada_stride) {
+                                                              long ada_stride, float* __restrict__ qscale) {
+  constexpr bool Q8 = sizeof(TY) == 1;
   constexpr int MAXV = 8;  // float4 per lane: 8 * 4 * 64 = 2048 columns
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -138,7 +142,11 @@ __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict_
         o[2] = o[2] * (1.0f + sc.z) + sh.z;
         o[3] = o[3] * (1.0f + sc.w) + sh.w;
       }
-      if (sizeof(TY) == 4) {
+      if constexpr (Q8) {
+        const uint32_t b01 = bf16x2_bits(o[0], o[1]), b23 = bf16x2_bits(o[2], o[3]);
+        v[i] = make_float4(bf16_to_f(b01 & 0xFFFFu), bf16_to_f(b01 >> 16), bf16_to_f(b23 & 0xFFFFu),
+                           bf16_to_f(b23 >> 16));
+      } else if (sizeof(TY) == 4) {
         *(float4*)((float*)yr + c) = make_float4(o[0], o[1], o[2], o[3]);
       } else {
         *(uint2*)((uint16_t*)yr + c) = make_uint2(bf16x2_bits(o[0], o[1]),
@@ -146,36 +154,61 @@ __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict_
       }
     }
   }
+  if constexpr (Q8) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (4 * lane + 256 * i < D)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    amax = wave_max(amax);
+    const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (lane == 0) qscale[row] = sc;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = 4 * lane + 256 * i;
+      if (c < D) {
+        int q = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(v[i].x, sc), __fdiv_rn(v[i].y, sc), 0, false);
+        q = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(v[i].z, sc), __fdiv_rn(v[i].w, sc), q, true);
+        *(uint32_t*)((uint8_t*)yr + c) = (uint32_t)q;
+      }
+    }
+  }
 }
 
 template <typename TY>
 static hipError_t resid_ln_go(float* h, const float* partials, int nsplit, long split_stride, TY* y, int rows, int D,
-                              const float* ada, int ada_rows, long ada_stride, hipStream_t s) {
+                              const float* ada, int ada_rows, long ada_stride, float* qscale, hipStream_t s) {
   dim3 grid((rows + 3) / 4), blk(256);
   switch (nsplit) {
-    case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 1: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 1>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 2: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 2>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 3: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 3>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 4: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 4>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 5: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 5>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 6: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 6>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 7: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 7>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
-    case 8: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 8>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride); break;
+    case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 1: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 1>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 2: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 2>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 3: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 3>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 4: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 4>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 5: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 5>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 6: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 6>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 7: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 7>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
+    case 8: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 8>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_resid_layernorm(float* h, const float* partials, int nsplit, long split_stride, void* y, DType yt,
-                                  int rows, int D, const float* ada, hipStream_t s, int ada_rows, long ada_stride) {
+                                  int rows, int D, const float* ada, hipStream_t s, int ada_rows, long ada_stride,
+                                  float* qscale) {
   if (rows <= 0) return hipSuccess;
   if (D > 2048 || (D % 4) != 0 || ada_rows < 0) return hipErrorInvalidValue;
   if (!partials) nsplit = 0;
   if (yt == DT_F32)
-    return resid_ln_go<float>(h, partials, nsplit, split_stride, (float*)y, rows, D, ada, ada_rows, ada_stride, s);
+    return resid_ln_go<float>(h, partials, nsplit, split_stride, (float*)y, rows, D, ada, ada_rows, ada_stride, nullptr,
+                              s);
   if (yt == DT_BF16)
-    return resid_ln_go<bf16>(h, partials, nsplit, split_stride, (bf16*)y, rows, D, ada, ada_rows, ada_stride, s);
+    return resid_ln_go<bf16>(h, partials, nsplit, split_stride, (bf16*)y, rows, D, ada, ada_rows, ada_stride, nullptr,
+                             s);
+  if (yt == DT_FP8 && qscale)
+    return resid_ln_go<uint8_t>(h, partials, nsplit, split_stride, (uint8_t*)y, rows, D, ada, ada_rows, ada_stride,
+                                qscale, s);
   return hipErrorInvalidValue;
 }
 

@@ -35,6 +35,30 @@ def test_repeat_and_graph_bitwise(wl):
     assert np.array_equal(y_eager, y_g1)
 
 
+def test_w8a8_graph_replays_and_masked_tokens_bitwise():
+    # W8A8 on the ragged B=64 recipe: eager, then three graph replays with eager work of the
+    # same handle (a velocity call) and synchronisations between them, all bitwise equal; and
+    # masked VL tokens changed to huge values leave the result bitwise unchanged (they are
+    # neither quantised nor projected)
+    w = small("dit32_bf16_b64", batch=8)
+    w = replace(w, name=w.name + "_fp8a8", cfg=replace(w.cfg, precision="fp8a8"))
+    wt, inp, nz = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    h = build_head(w, wt, flags=H.FLAG_USE_GRAPH)
+    y_eager = gpu_action(h, inp, nz)
+    ys = [gpu_action(h, inp, nz, prepare=True)]
+    for k in (1, 2):
+        gpu_velocity(h, inp, nz, k)
+        ys.append(gpu_action(h, inp, nz))
+    for y in ys:
+        assert np.array_equal(y, y_eager)
+    inp2 = dict(inp)
+    vl = inp["vl_features"].copy()
+    vl[inp["vl_mask"] == 0] = 1000.0
+    inp2["vl_features"] = vl
+    assert np.array_equal(gpu_action(h, inp2, nz), y_eager)
+    h.close()
+
+
 def test_batch_independence(wl):
     # a sample alone equals the same sample inside the batch; the GEMM tiling and split-K
     # depth depend on the batch size, so only the fp32 summation order may differ

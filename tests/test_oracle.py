@@ -468,6 +468,19 @@ def test_row_quantisation():
     assert np.array_equal(O.quantize_e4m3_rows(v), v)
 
 
+def test_row_quantisation_edge_codes():
+    # amax 448 (scale exactly 1): -0 keeps its sign, magnitudes below half the smallest
+    # subnormal (2^-10) round to a signed zero, exactly half rounds to the even code 0, the
+    # midpoint 2^-10 * 3 between subnormals 1 and 2 goes to the even code 2, 448 is 0x7E
+    row = np.array([[448.0, -0.0, -1e-30, 2.0 ** -10, 3 * 2.0 ** -10, -448.0, 1.0]])
+    codes, scales = O.quantize_e4m3_rows_codes(row)
+    assert scales.tolist() == [1.0]
+    assert codes.tolist() == [[0x7E, 0x80, 0x80, 0x00, 0x02, 0xFE, 0x38]]
+    # a row of equal magnitudes maps every entry to +-448
+    codes, scales = O.quantize_e4m3_rows_codes(np.array([[-3.0, 3.0, 3.0]]))
+    assert codes.tolist() == [[0xFE, 0x7E, 0x7E]] and scales[0] == np.float32(3.0) / np.float32(448.0)
+
+
 def test_w8a8_linear_is_exact_on_representable_operands():
     # inputs and weights on the e4m3 grid with row / column amax 448: both quantisations are the
     # identity, so the fp8a8 linear is the exact product (integer-valued, checked by brute force)

@@ -59,6 +59,27 @@ def test_w8a8_graph_replays_and_masked_tokens_bitwise():
     h.close()
 
 
+def test_w8a8_bad_id_stays_in_its_sample():
+    # non-strict mode, W8A8: the NaN rows of a sample with an invalid id are quantised row by
+    # row, so the other samples are bitwise those of the clean call
+    w = small("dit32_bf16_b64", batch=8)
+    w = replace(w, name=w.name + "_fp8a8", cfg=replace(w.cfg, precision="fp8a8"))
+    wt, inp, nz = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    h = build_head(w, wt)
+    y = gpu_action(h, inp, nz)
+    bad = dict(inp)
+    bad["embodiment_id"] = inp["embodiment_id"].copy()
+    bad["embodiment_id"][5] = w.cfg.num_categories
+    yb = gpu_action(h, bad, nz)
+    assert np.all(np.isnan(yb[5]))
+    keep = [b for b in range(w.batch) if b != 5]
+    assert np.array_equal(yb[keep], y[keep])
+    with pytest.raises(H.Gr00tError) as e:
+        gpu_action(h, inp, nz)
+    assert e.value.status == "E_DEVICE_ERROR"
+    h.close()
+
+
 def test_batch_independence(wl):
     # a sample alone equals the same sample inside the batch; the GEMM tiling and split-K
     # depth depend on the batch size, so only the fp32 summation order may differ

@@ -498,3 +498,144 @@ def test_w8a8_linear_is_exact_on_representable_operands():
     # bf16 mode leaves the input as it is
     xr = rng.standard_normal((2, 9))
     assert np.array_equal(O.dit_linear({"precision": "bf16"}, xr, w, b), O.linear(xr, w, b))
+
+
+# ---------------------------------------------------------------- encoders, decoder and output head
+# Closed forms with hand-chosen weights: each expected value is written out from the
+# definitions on the pages, so that a dropped activation, a swapped concatenation or a
+# missing output projection in the oracle changes the result.
+
+def _swish(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def _sin_cos(tau, dim):
+    half = dim // 2
+    w = 10000.0 ** (-np.arange(half) / half)
+    return np.concatenate([np.sin(tau * w), np.cos(tau * w)])
+
+
+def test_timestep_encoder_closed_form():
+    # "Model architecture", Diffusion transformer (DiT): a sinusoidal timestep embedding
+    # through the timestep encoder (reading R4: Linear -> SiLU -> Linear). With W1 picking
+    # sin(tau * w_0) = sin(tau) into every unit, W2 = 2 I and biases b1, b2:
+    # temb = 2 * SiLU(sin(tau) + b1) + b2.
+    T, D = 16, 6
+    b1 = np.array([0.0, 1.0, -1.0, 2.0, -3.0, 0.5])
+    b2 = np.full(D, 0.25)
+    w1 = np.zeros((T, D))
+    w1[0, :] = 1.0
+    P = {"time.w1": w1, "time.b1": b1, "time.w2": 2.0 * np.eye(D), "time.b2": b2}
+    cfg = {"time_freq_dim": T}
+    for tau in (0, 250, 875):
+        got = O.timestep_encoder(P, cfg, tau)
+        want = 2.0 * _swish(math.sin(tau) + b1) + b2
+        assert np.allclose(got, want, rtol=0, atol=1e-14), tau
+    # the cos half enters too: W1 picking cos(tau * w_0) gives SiLU(cos(tau) + b1)
+    w1 = np.zeros((T, D))
+    w1[T // 2, :] = 1.0
+    P["time.w1"] = w1
+    assert np.allclose(O.timestep_encoder(P, cfg, 250), 2.0 * _swish(math.cos(250) + b1) + b2, rtol=0, atol=1e-14)
+
+
+def test_action_encoder_concat_order_and_swish():
+    # "Model architecture", Embodiment-specific projectors > Multi-embodiment action encoder:
+    # a = W1(x); the timestep encoding is concatenated after a; swish(W2(.)); W3(.).
+    # W1 copies x into the first A units (+0.1), W2 = [I ; 3 I] (action rows, then timestep
+    # rows), W3 = 2 I + 0.25 per category c scaled by (c + 1):
+    #   af = (c + 1) * 2 * swish(a + 3 * sinD(tau) + b2) + 0.25
+    B, H, A, D, C = 2, 3, 4, 8, 2
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((B, H, A))
+    ids = np.array([1, 0])
+    w1 = np.zeros((C, A, D))
+    w1[:, :, :A] = np.eye(A)
+    b2 = rng.standard_normal((C, D)) * 0.5
+    P = {"action_enc.w1": w1, "action_enc.b1": np.full((C, D), 0.1),
+         "action_enc.w2": np.stack([np.concatenate([np.eye(D), 3.0 * np.eye(D)])] * C), "action_enc.b2": b2,
+         "action_enc.w3": np.stack([2.0 * (c + 1) * np.eye(D) for c in range(C)]),
+         "action_enc.b3": np.full((C, D), 0.25)}
+    cfg = {"hidden": D}
+    for tau in (0, 500):
+        got = O.action_encoder(P, cfg, x, tau, ids)
+        te = _sin_cos(tau, D)
+        for b in range(B):
+            c = ids[b]
+            a = np.full((H, D), 0.1)
+            a[:, :A] += x[b]
+            want = 2.0 * (c + 1) * _swish(a + 3.0 * te + b2[c]) + 0.25
+            assert np.allclose(got[b], want, rtol=0, atol=1e-13), (tau, b)
+
+
+def test_state_encoder_relu_between_linears():
+    # "Model architecture", Action head architecture > Components: the state encoder is a
+    # per-embodiment MLP (reading R13: Linear_c -> ReLU -> Linear_c). W1 copies the state
+    # into the first Sd units with bias -0.5, W2 = -(c + 1) I with bias 0.125:
+    #   s = -(c + 1) * max(state - 0.5, 0) + 0.125 on the first Sd units,
+    #   s = -(c + 1) * max(-0.5, 0) + 0.125 = 0.125 on the rest.
+    B, Sd, D, C = 3, 4, 6, 3
+    rng = np.random.default_rng(12)
+    state = rng.standard_normal((B, 1, Sd))
+    ids = np.array([2, 0, 1])
+    w1 = np.zeros((C, Sd, D))
+    w1[:, :, :Sd] = np.eye(Sd)
+    P = {"state_enc.w1": w1, "state_enc.b1": np.full((C, D), -0.5),
+         "state_enc.w2": np.stack([-(c + 1.0) * np.eye(D) for c in range(C)]),
+         "state_enc.b2": np.full((C, D), 0.125)}
+    got = O.state_encoder(P, state, ids)
+    for b in range(B):
+        want = np.full(D, 0.125)
+        want[:Sd] = -(ids[b] + 1.0) * np.maximum(state[b, 0] - 0.5, 0.0) + 0.125
+        assert np.allclose(got[b, 0], want, rtol=0, atol=1e-15), b
+    assert np.any(state[..., :] < 0.5)  # the ReLU is exercised
+
+
+def test_action_decoder_relu_between_linears():
+    # "Model architecture", Action head architecture > Components: the action decoder is a
+    # per-embodiment MLP to action_dim (reading R13). W1 = I with bias -0.5, W2 takes the
+    # first A units times -(c + 1), bias 0.125:  v = -(c + 1) * max(y[:A] - 0.5, 0) + 0.125.
+    B, H, D, A, C = 2, 3, 6, 4, 2
+    rng = np.random.default_rng(13)
+    y = rng.standard_normal((B, H, D))
+    ids = np.array([1, 0])
+    w2 = np.zeros((C, D, A))
+    for c in range(C):
+        w2[c, :A, :] = -(c + 1.0) * np.eye(A)
+    P = {"action_dec.w1": np.stack([np.eye(D)] * C), "action_dec.b1": np.full((C, D), -0.5),
+         "action_dec.w2": w2, "action_dec.b2": np.full((C, A), 0.125)}
+    got = O.action_decoder(P, y, ids)
+    for b in range(B):
+        want = -(ids[b] + 1.0) * np.maximum(y[b, :, :A] - 0.5, 0.0) + 0.125
+        assert np.allclose(got[b], want, rtol=0, atol=1e-15), b
+
+
+def test_dit_output_head_is_modulated_norm_then_projection():
+    # reading R2 ("Model architecture", Diffusion transformer (DiT): output_dim): after the
+    # blocks, a LayerNorm without affine modulated by [scale | shift] = Linear(SiLU(temb)),
+    # then a D -> D projection. Blocks with zero output projections pass h through; with
+    # out.ada.w = 0, out.ada.b = [sc | sh], out.proj.w = 3 I, out.proj.b = bp:
+    #   y = 3 * ((h - mean) / sqrt(var + 1e-5) * (1 + sc) + sh) + bp.
+    w = tiny_workload()
+    cfg = w.cfg.as_dict()
+    D = w.cfg.hidden
+    wt = synth.make_weights(w)
+    for l in range(w.cfg.num_layers):
+        for n in ("attn.wo", "attn.bo", "ff.w2", "ff.b2"):
+            wt[f"blocks.{l}.{n}"][:] = 0
+    rng = np.random.default_rng(14)
+    # float32 values, as the weight tensors hold them
+    sc, sh, bp = (rng.standard_normal(D).astype(np.float32).astype(np.float64) for _ in range(3))
+    wt["out.ada.w"][:] = 0
+    wt["out.ada.b"][:] = np.concatenate([sc, sh])
+    wt["out.proj.w"][:] = 3.0 * np.eye(D)
+    wt["out.proj.b"][:] = bp
+    P = O.effective_params(cfg, wt)
+    B, S = 2, 5
+    h = rng.standard_normal((B, S, D)) * 2.0 + 0.3
+    vl = rng.standard_normal((B, 7, w.cfg.vl_dim))
+    valid = np.ones((B, 7), bool)
+    got = O.dit(P, cfg, h, vl, valid, None, rng.standard_normal(D))
+    mu = h.mean(axis=-1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=-1, keepdims=True)
+    want = 3.0 * ((h - mu) / np.sqrt(var + 1e-5) * (1.0 + sc) + sh) + bp
+    assert np.allclose(got, want, rtol=0, atol=1e-12)

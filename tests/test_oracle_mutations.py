@@ -119,6 +119,55 @@ def _training_target_sign(cfg, weights, inputs, actions, noise, t, params=None):
     return O.__dict__["_orig_training_loss"](cfg, weights, inputs, noise, actions, 1.0 - np.asarray(t), params)
 
 
+def _timestep_encoder_no_silu(P, cfg, tau):
+    e = O.sinusoid(np.array(float(tau)), cfg["time_freq_dim"])
+    return O.linear(O.linear(e, P["time.w1"], P["time.b1"]), P["time.w2"], P["time.b2"])
+
+
+def _action_encoder_concat_swapped(P, cfg, x, tau, ids):
+    B, H, _ = x.shape
+    a = O.category_linear(x, P["action_enc.w1"], P["action_enc.b1"], ids)
+    te = np.broadcast_to(O.sinusoid(np.array(float(tau)), cfg["hidden"]), (B, H, cfg["hidden"]))
+    z = O.silu(O.category_linear(np.concatenate([te, a], axis=-1), P["action_enc.w2"], P["action_enc.b2"], ids))
+    return O.category_linear(z, P["action_enc.w3"], P["action_enc.b3"], ids)
+
+
+def _action_encoder_swish_after_w3(P, cfg, x, tau, ids):
+    B, H, _ = x.shape
+    a = O.category_linear(x, P["action_enc.w1"], P["action_enc.b1"], ids)
+    te = np.broadcast_to(O.sinusoid(np.array(float(tau)), cfg["hidden"]), (B, H, cfg["hidden"]))
+    z = O.category_linear(np.concatenate([a, te], axis=-1), P["action_enc.w2"], P["action_enc.b2"], ids)
+    return O.silu(O.category_linear(z, P["action_enc.w3"], P["action_enc.b3"], ids))
+
+
+def _state_encoder_no_relu(P, state, ids):
+    z = O.category_linear(state, P["state_enc.w1"], P["state_enc.b1"], ids)
+    return O.category_linear(z, P["state_enc.w2"], P["state_enc.b2"], ids)
+
+
+def _action_decoder_no_relu(P, y, ids):
+    z = O.category_linear(y, P["action_dec.w1"], P["action_dec.b1"], ids)
+    return O.category_linear(z, P["action_dec.w2"], P["action_dec.b2"], ids)
+
+
+def _dit_plain_final_norm(P, cfg, sa_embs, vl, valid, image, temb):
+    h = sa_embs
+    for l in range(cfg["num_layers"]):
+        masks = None if l % 2 else [O.cross_layer_mask(cfg, l, valid[b], None if image is None else image[b])
+                                    for b in range(h.shape[0])]
+        h = O.transformer_block(P, cfg, l, h, vl, masks, temb)
+    return O.dit_linear(cfg, O.layer_norm(h), P["out.proj.w"], P["out.proj.b"])
+
+
+def _dit_no_output_projection(P, cfg, sa_embs, vl, valid, image, temb):
+    h = sa_embs
+    for l in range(cfg["num_layers"]):
+        masks = None if l % 2 else [O.cross_layer_mask(cfg, l, valid[b], None if image is None else image[b])
+                                    for b in range(h.shape[0])]
+        h = O.transformer_block(P, cfg, l, h, vl, masks, temb)
+    return O.ada_layer_norm(P, "out.", h, temb)
+
+
 CASES = [
     ("gelu", _gelu_tanh, pins.test_gelu_textbook_values),
     ("attention", _attention_no_temperature, pins.test_attention_temperature),
@@ -139,6 +188,13 @@ CASES = [
     ("discretize_t", _bucket_rounded, pins.test_training_bucket_matches_inference_grid),
     ("training_loss", _training_target_sign, pins.test_training_loss_closed_form),
     ("quantize_e4m3_rows", _rows_quantised_per_column, pins.test_row_quantisation),
+    ("timestep_encoder", _timestep_encoder_no_silu, pins.test_timestep_encoder_closed_form),
+    ("action_encoder", _action_encoder_concat_swapped, pins.test_action_encoder_concat_order_and_swish),
+    ("action_encoder", _action_encoder_swish_after_w3, pins.test_action_encoder_concat_order_and_swish),
+    ("state_encoder", _state_encoder_no_relu, pins.test_state_encoder_relu_between_linears),
+    ("action_decoder", _action_decoder_no_relu, pins.test_action_decoder_relu_between_linears),
+    ("dit", _dit_plain_final_norm, pins.test_dit_output_head_is_modulated_norm_then_projection),
+    ("dit", _dit_no_output_projection, pins.test_dit_output_head_is_modulated_norm_then_projection),
 ]
 
 

@@ -117,6 +117,7 @@ struct Ws {  // workspace pointers
   void *n, *q, *k, *v, *o, *u, *y, *e1, *e2, *se1, *vln, *kc, *vc;
   float *x, *s, *vout, *part;
   uint8_t *code, *bad;
+  unsigned* bad_count;  // monotonic count of invalid ids met on the device (never cleared)
   int *ids, *iota, *vrow, *vcount;
   float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
   uint8_t* q8;  // W8A8: e4m3 input rows of the current GEMM
@@ -141,9 +142,20 @@ struct gr00t_head {
   hipStream_t cap_stream = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   uint64_t calls = 0;
-  uint8_t* bad_host = nullptr;      // pinned copy of the per-sample bad-id flags
-  hipEvent_t bad_event = nullptr;
-  int bad_pending_B = 0;
+  // Deferred report of invalid ids (non-strict mode). Every call copies the device count of
+  // invalid ids met so far and its per-sample flags into the next of kReportSlots pinned slots
+  // and records an event. The count only grows, so any completed copy taken after a bad call
+  // shows it, however many calls were enqueued in between; a count above bad_reported is
+  // reported once by the next call that finds such a completed copy.
+  static constexpr int kReportSlots = 4;
+  struct ReportSlot {
+    uint8_t* host = nullptr;  // [4 bytes count][max_batch flags]
+    hipEvent_t ev = nullptr;
+    bool recorded = false;
+    int B = 0;
+  } rep[kReportSlots];
+  int rep_next = 0;
+  uint32_t bad_reported = 0;
   // (B, L_pad) of the VL key/value caches and key masks in the workspace: those of the last
   // call that ran the full prologue (0, 0: none yet)
   int kv_B = 0, kv_L = 0;
@@ -209,6 +221,31 @@ int check_config(const gr00t_config* c, std::string& why) {
   if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8)) return bad("unknown flag bits");
   if ((c->flags & GR00T_FLAG_W8A8) && c->weight_dtype != GR00T_FP8_E4M3)
     return bad("GR00T_FLAG_W8A8 needs FP8_E4M3 weights");
+  // The kernels address each GEMM operand, cache layer and workspace buffer through a 32-bit
+  // buffer descriptor with 32-bit offsets: every such operand must stay below 2^31 - 16 bytes.
+  {
+    const double Bm = c->max_batch, Lm = c->max_vl_len, Lmp = (c->max_vl_len + 31) / 32 * 32.0;
+    const double D = c->hidden, F = c->ff_dim, E = c->vl_dim, S = c->action_horizon + 1.0;
+    const double C = c->num_categories, Nl = c->num_layers, Nc = (c->num_layers + 1) / 2;
+    const double ab = c->act_dtype == GR00T_F32 ? 4.0 : 2.0, wb = c->weight_dtype == GR00T_F32 ? 4.0 : 2.0;
+    const double limit = 2147483632.0;  // 0x7FFFFFF0
+    const struct { const char* what; double bytes; } ops[] = {
+        {"the VL features and K/V projection input (max_batch * max_vl_len * vl_dim)", Bm * Lm * E * ab},
+        {"one cross block's key or value cache (max_batch * max_vl_len * hidden)", Bm * Lmp * D * ab},
+        {"the MLP activations (max_batch * (action_horizon + 1) * ff_dim)", Bm * S * F * ab},
+        {"the split-K partial sums (8 * max_batch * (action_horizon + 1) * hidden)", 8.0 * Bm * S * D * 4.0},
+        {"the K/V projection weights (cross blocks * 2 * hidden * vl_dim)", Nc * 2.0 * D * E * wb},
+        {"one MLP weight matrix (ff_dim * hidden)", F * D * wb},
+        {"the adaLN weights ((num_layers + 1) * 2 * hidden * hidden)", (Nl + 1.0) * 2.0 * D * D * wb},
+        {"one per-embodiment weight table (num_categories * hidden * hidden)", C * D * D * wb},
+    };
+    for (const auto& o : ops)
+      if (o.bytes > limit) {
+        why = std::string("capacity too large: ") + o.what + " would take " + std::to_string((long long)o.bytes) +
+              " bytes, above the 2^31 - 16 bytes one buffer descriptor addresses";
+        return GR00T_E_INVALID_ARG;
+      }
+  }
   return GR00T_OK;
 }
 
@@ -687,7 +724,8 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s, bool reus
   const DType A = h->act;
   const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
   const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
-  LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s));
+  LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s,
+                                            h->w.bad_count));
   if (!reuse_vl) {
     h->kv_B = h->kv_L = 0;  // no valid cache until the projection below is enqueued
     LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
@@ -979,13 +1017,27 @@ int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out, bool re
 
 // Strict-mode id check on the host, and the deferred report of bad ids seen on the device.
 int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
-  if (h->bad_pending_B > 0 && hipEventQuery(h->bad_event) == hipSuccess) {
-    const int nb = h->bad_pending_B;
-    h->bad_pending_B = 0;
-    for (int b = 0; b < nb; ++b)
-      if (h->bad_host[b])
-        return fail(h, GR00T_E_DEVICE_ERROR, "a previous call met an embodiment id outside [0, num_categories) "
-                                             "at sample " + std::to_string(b) + "; its rows were set to NaN");
+  uint32_t newest = h->bad_reported;
+  int sample = -1;
+  for (auto& r : h->rep) {
+    if (!r.recorded || hipEventQuery(r.ev) != hipSuccess) continue;
+    uint32_t cnt;
+    std::memcpy(&cnt, r.host, 4);
+    if ((int32_t)(cnt - newest) > 0) {
+      newest = cnt;
+      sample = -1;
+      for (int b = 0; b < r.B && sample < 0; ++b)
+        if (r.host[4 + b]) sample = b;
+    }
+  }
+  (void)hipGetLastError();  // a not-ready query leaves no error behind
+  if (newest != h->bad_reported) {
+    const uint32_t n = newest - h->bad_reported;
+    h->bad_reported = newest;
+    return fail(h, GR00T_E_DEVICE_ERROR,
+                "an earlier call met " + std::to_string(n) + " embodiment id(s) outside [0, num_categories)" +
+                    (sample >= 0 ? " (sample " + std::to_string(sample) + " of the call whose report was read)" : "") +
+                    "; the rows of those samples were set to NaN");
   }
   if (h->cfg.flags & GR00T_FLAG_STRICT) {
     std::vector<int32_t> ids(in->batch);
@@ -996,6 +1048,18 @@ int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
         return fail(h, GR00T_E_EMBODIMENT, "embodiment_id[" + std::to_string(b) + "] = " + std::to_string(ids[b]) +
                                                " outside [0, " + std::to_string(h->cfg.num_categories) + ")");
   }
+  return GR00T_OK;
+}
+
+// Enqueue the copy of the invalid-id count and this call's per-sample flags into the next report slot.
+int enqueue_report(gr00t_head* h, int B, hipStream_t s) {
+  auto& r = h->rep[h->rep_next];
+  h->rep_next = (h->rep_next + 1) % gr00t_head::kReportSlots;
+  HIPCHK(h, hipMemcpyAsync(r.host, h->w.bad_count, 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(h, hipMemcpyAsync(r.host + 4, h->w.bad, B, hipMemcpyDeviceToHost, s));
+  HIPCHK(h, hipEventRecord(r.ev, s));
+  r.recorded = true;
+  r.B = B;
   return GR00T_OK;
 }
 
@@ -1112,6 +1176,7 @@ int gr00t_finalize(gr00t_head* h) {
       {(void**)&h->w.s, Bm * D * 4},          {(void**)&h->w.vout, Bm * H * A * 4},
       {(void**)&h->w.part, 8 * Bm * S * D * 4},
       {(void**)&h->w.code, Bm * Lm},          {(void**)&h->w.bad, Bm},           {(void**)&h->w.ids, Bm * 4},
+      {(void**)&h->w.bad_count, 4},
       {(void**)&h->w.vrow, Bm * Lm * 4},      {(void**)&h->w.vcount, 4},
       {(void**)&h->w.iota, C * 4},            {(void**)&h->w.sin_t, K * T * 4},  {(void**)&h->w.t1, K * D * 4},
       {(void**)&h->w.temb, K * D * 4},        {(void**)&h->w.stemb, K * D * 4},
@@ -1136,14 +1201,17 @@ int gr00t_finalize(gr00t_head* h) {
   for (size_t i = 0; i < C; ++i) iota[i] = (int)i;
   HIPCHK(h, hipMemcpy(h->w.iota, iota.data(), C * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemset(h->w.bad, 0, Bm));
+  HIPCHK(h, hipMemset(h->w.bad_count, 0, 4));
   // key/value padding rows and columns are read with weight 0: keep them finite
   HIPCHK(h, hipMemset(h->w.kc, 0, Nc * Bm * Lmp * D * ab));
   HIPCHK(h, hipMemset(h->w.vc, 0, Nc * Bm * Lmp * D * ab));
   HIPCHK(h, hipMemset(h->w.k, 0, Bm * Sp * D * ab));
   HIPCHK(h, hipMemset(h->w.v, 0, Bm * Sp * D * ab));
   HIPCHK(h, hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
-  HIPCHK(h, hipHostMalloc((void**)&h->bad_host, Bm, hipHostMallocDefault));
-  HIPCHK(h, hipEventCreateWithFlags(&h->bad_event, hipEventDisableTiming));
+  for (auto& r : h->rep) {
+    HIPCHK(h, hipHostMalloc((void**)&r.host, 4 + Bm, hipHostMallocDefault));
+    HIPCHK(h, hipEventCreateWithFlags(&r.ev, hipEventDisableTiming));
+  }
   int rc = build_tables(h, h->cap_stream);
   if (rc != GR00T_OK) return rc;
   HIPCHK(h, hipStreamSynchronize(h->cap_stream));
@@ -1203,9 +1271,8 @@ static int get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
   }
   LAUNCH(h, s, K_SMALL, launch_output(h->w.x, in->action_mask, h->w.bad, action_pred, in->batch,
                           h->cfg.action_horizon * h->cfg.action_dim, s));
-  HIPCHK(h, hipMemcpyAsync(h->bad_host, h->w.bad, in->batch, hipMemcpyDeviceToHost, s));
-  HIPCHK(h, hipEventRecord(h->bad_event, s));
-  h->bad_pending_B = in->batch;
+  rc = enqueue_report(h, in->batch, s);
+  if (rc != GR00T_OK) return rc;
   h->calls++;
   return GR00T_OK;
 }
@@ -1239,9 +1306,8 @@ int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* acti
   if (rc != GR00T_OK) return rc;
   LAUNCH(h, s, K_SMALL, launch_masked_mse(h->w.vout, actions, in->noise, in->action_mask, h->w.bad, B, per, loss, s));
   if (v_pred) HIPCHK(h, hipMemcpyAsync(v_pred, h->w.vout, sizeof(float) * B * per, hipMemcpyDeviceToDevice, s));
-  HIPCHK(h, hipMemcpyAsync(h->bad_host, h->w.bad, B, hipMemcpyDeviceToHost, s));
-  HIPCHK(h, hipEventRecord(h->bad_event, s));
-  h->bad_pending_B = B;
+  rc = enqueue_report(h, B, s);
+  if (rc != GR00T_OK) return rc;
   h->calls++;
   return GR00T_OK;
 }
@@ -1283,15 +1349,20 @@ int gr00t_quantize_e4m3_rows(gr00t_head* h, const void* x, int64_t ld_x, int32_t
 
 void gr00t_destroy(gr00t_head* h) {
   if (!h) return;
-  if (h->finalized || h->arena || h->wsbase) (void)hipSetDevice(h->device);
+  if (h->finalized || h->arena || h->wsbase) {
+    (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();  // copies into the pinned report slots may still be in flight
+  }
   for (auto& kv : h->graphs) (void)hipGraphExecDestroy(kv.second);
   if (h->cap_stream) {
     (void)hipStreamSynchronize(h->cap_stream);
     (void)hipStreamDestroy(h->cap_stream);
   }
-  if (h->bad_event) (void)hipEventDestroy(h->bad_event);
+  for (auto& r : h->rep) {
+    if (r.ev) (void)hipEventDestroy(r.ev);
+    if (r.host) (void)hipHostFree(r.host);
+  }
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
-  if (h->bad_host) (void)hipHostFree(h->bad_host);
   if (h->tr_base) (void)hipFree(h->tr_base);
   if (h->arena || h->wsbase) (void)hipDeviceSynchronize();
   if (h->arena) (void)hipFree(h->arena);

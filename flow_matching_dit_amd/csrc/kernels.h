@@ -136,9 +136,10 @@ hipError_t launch_attention(const AttnArgs& a, DType t, hipStream_t s);
 // blocks. Without an image mask both bits equal the valid bit.
 hipError_t launch_mask_codes(const uint8_t* vl_mask, const uint8_t* image_mask, uint8_t* code, int n,
                              hipStream_t s);
-// ids_out[b] = ids_in[b] if in [0, C) else 0; bad[b] = out of range.
+// ids_out[b] = ids_in[b] if in [0, C) else 0; bad[b] = out of range; *bad_count (when given) is
+// increased by the number of out-of-range ids (a monotonic count across calls).
 hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C,
-                               hipStream_t s);
+                               hipStream_t s, unsigned* bad_count = nullptr);
 // dst rows (b * dst_stride_rows + dst_row_off) <- src rows b (fp32, width D).
 hipError_t launch_copy_rows(const float* src, long src_ld, float* dst, long dst_ld, long dst_gstride,
                             int dst_row_off, int B, int D, hipStream_t s);

@@ -726,17 +726,21 @@ hipError_t launch_compact_rows(const uint8_t* code, int n, int* idx, int* count,
   return hipGetLastError();
 }
 
-__global__ void sanitize_ids_kernel(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C) {
+__global__ void sanitize_ids_kernel(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C,
+                                    unsigned* bad_count) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int id = ids_in[b];
   const bool ok = id >= 0 && id < C;
   ids_out[b] = ok ? id : 0;
   bad[b] = ok ? 0 : 1;
+  if (!ok && bad_count) atomicAdd(bad_count, 1u);
 }
 
-hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C, hipStream_t s) {
-  hipLaunchKernelGGL(sanitize_ids_kernel, dim3((B + 255) / 256), dim3(256), 0, s, ids_in, ids_out, bad, B, C);
+hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C, hipStream_t s,
+                               unsigned* bad_count) {
+  hipLaunchKernelGGL(sanitize_ids_kernel, dim3((B + 255) / 256), dim3(256), 0, s, ids_in, ids_out, bad, B, C,
+                     bad_count);
   return hipGetLastError();
 }
 

@@ -130,6 +130,27 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(name, t, shape, dtypes, device, optional=False):
+    """Raise ValueError unless tensor t has this shape, one of these dtypes, is contiguous and
+    lives on `device` (the library reads raw pointers: a wrong dtype or a short buffer would be
+    read as garbage or past its end)."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the head's device is {device}")
+
+
 class Gr00tHead:
     """One library handle: create -> load_weights -> finalize -> [prepare] -> get_action."""
 
@@ -173,9 +194,37 @@ class Gr00tHead:
         self._check(self.lib.gr00t_prepare(self.h, batch, vl_len))
         return self
 
+    @property
+    def torch_device(self):
+        import torch
+        return torch.device("cuda", self.device)
+
+    def _check_inputs(self, B, L, vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask,
+                      state_features_out=None, need_vl=True, need_noise=False):
+        """Shapes, dtypes and device of one call's tensors against the handle's configuration."""
+        import torch
+        c = self._c
+        u8 = (torch.uint8, torch.bool)
+        H, A = c.action_horizon, c.action_dim
+        # shapes and dtypes of every tensor first, then the device
+        for dev in (None, self.torch_device):
+            _expect("vl_features", vl_features, (B, L, c.vl_dim), (self.act_torch_dtype,), dev, optional=not need_vl)
+            _expect("vl_mask", vl_mask, (B, L), u8, dev, optional=True)
+            _expect("image_mask", image_mask, (B, L), u8, dev, optional=True)
+            _expect("state", state, (B, 1, c.state_dim), (torch.float32,), dev)
+            _expect("embodiment_id", embodiment_id, (B,), (torch.int32,), dev)
+            _expect("noise", noise, (B, H, A), (torch.float32,), dev, optional=not need_noise)
+            _expect("action_mask", action_mask, (B, H, A), u8, dev, optional=True)
+            _expect("state_features_out", state_features_out, (B, 1, c.hidden), (torch.float32,), dev,
+                    optional=True)
+
     def _inputs(self, vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask,
-                state_features_out) -> Gr00tInputs:
+                state_features_out, need_noise=False) -> Gr00tInputs:
+        if getattr(vl_features, "dim", lambda: 0)() != 3:
+            raise ValueError("vl_features must be a 3-D tensor [B, L, vl_dim]")
         B, L = int(vl_features.shape[0]), int(vl_features.shape[1])
+        self._check_inputs(B, L, vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask,
+                           state_features_out, need_noise=need_noise)
         return Gr00tInputs(B, L, _ptr(vl_features), _ptr(vl_mask), _ptr(image_mask), _ptr(state),
                            _ptr(embodiment_id), _ptr(noise), _ptr(action_mask), _ptr(state_features_out))
 
@@ -189,11 +238,13 @@ class Gr00tHead:
         """action_pred [B, H, A] f32 on the device (enqueued on the current stream)."""
         import torch
         B = int(vl_features.shape[0])
+        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask,
+                           state_features_out)
         if out is None:
             out = torch.empty((B, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
                               device=vl_features.device)
-        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask,
-                           state_features_out)
+        for dev in (None, self.torch_device):
+            _expect("out", out, (B, self._c.action_horizon, self._c.action_dim), (torch.float32,), dev)
         self._check(self.lib.gr00t_get_action(self.h, ctypes.byref(inp), c_void_p(out.data_ptr()),
                                               self._stream(stream)))
         return out
@@ -202,9 +253,12 @@ class Gr00tHead:
                             out=None, state_features_out=None, stream=None):
         """get_action with the VL key/value caches of the last full call of this (batch, vl_len)."""
         import torch
+        self._check_inputs(batch, vl_len, None, None, None, state, embodiment_id, noise, action_mask,
+                           state_features_out, need_vl=False)
         if out is None:
             out = torch.empty((batch, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
                               device=state.device)
+        _expect("out", out, (batch, self._c.action_horizon, self._c.action_dim), (torch.float32,), self.torch_device)
         inp = Gr00tInputs(batch, vl_len, None, None, None, _ptr(state), _ptr(embodiment_id), _ptr(noise),
                           _ptr(action_mask), _ptr(state_features_out))
         self._check(self.lib.gr00t_get_action_reuse_vl(self.h, ctypes.byref(inp), c_void_p(out.data_ptr()),
@@ -216,10 +270,14 @@ class Gr00tHead:
         """(loss [1] f32, v_pred [B, H, A] f32 or None) of the flow-matching training forward."""
         import torch
         B = int(vl_features.shape[0])
+        for dev in (None, self.torch_device):
+            _expect("actions", actions, (B, self._c.action_horizon, self._c.action_dim), (torch.float32,), dev)
+            _expect("t", t, (B,), (torch.float32,), dev)
+        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask, None,
+                           need_noise=True)
         loss = torch.empty(1, dtype=torch.float32, device=vl_features.device)
         vp = (torch.empty((B, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
                           device=vl_features.device) if v_pred else None)
-        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask, None)
         self._check(self.lib.gr00t_train_forward(self.h, ctypes.byref(inp), _ptr(actions), _ptr(t),
                                                  c_void_p(loss.data_ptr()), _ptr(vp), self._stream(stream)))
         return loss, vp
@@ -227,10 +285,11 @@ class Gr00tHead:
     def velocity(self, vl_features, vl_mask, image_mask, state, embodiment_id, noise, step_k: int,
                  stream=None):
         import torch
+        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, None, None,
+                           need_noise=True)
         B = int(vl_features.shape[0])
         out = torch.empty((B, self._c.action_horizon, self._c.action_dim), dtype=torch.float32,
                           device=vl_features.device)
-        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, None, None)
         self._check(self.lib.gr00t_velocity(self.h, ctypes.byref(inp), step_k, c_void_p(out.data_ptr()),
                                             self._stream(stream)))
         return out
@@ -239,8 +298,9 @@ class Gr00tHead:
         """Per-row e4m3 codes [rows, cols] uint8 and fp32 scales [rows] of a bf16 device matrix
         [rows, cols] (the W8A8 mode's quantisation of a GEMM input)."""
         import torch
-        if x.dtype != torch.bfloat16 or x.dim() != 2:
+        if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
             raise ValueError("x must be a 2-D bfloat16 tensor")
+        _expect("x", x, tuple(x.shape), (torch.bfloat16,), self.torch_device)
         rows, cols = int(x.shape[0]), int(x.shape[1])
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
         scale = torch.empty((rows,), dtype=torch.float32, device=x.device)

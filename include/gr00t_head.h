@@ -55,8 +55,13 @@ typedef enum gr00t_dtype {
 } gr00t_dtype;
 
 /* Flags of gr00t_config.flags. */
-#define GR00T_FLAG_STRICT 0x1u    /* validate ids on the host (one device->host copy) and
-                                     refuse unprepared shapes in graph mode */
+#define GR00T_FLAG_STRICT 0x1u    /* the Policy API's `strict` validation ("Understanding the
+                                     GR00T Policy API", Loading the Policy: observation shapes
+                                     and dtypes checked at run time, at a cost in speed): ids
+                                     are copied to the host and checked (E_EMBODIMENT) and, in
+                                     graph mode, an unprepared shape is refused (E_UNCAPTURED).
+                                     Shapes and dtypes of the tensors behind the pointers are
+                                     checked by the Python binding, which knows them. */
 #define GR00T_FLAG_USE_GRAPH 0x2u /* replay the K-step loop from a captured hipGraph */
 #define GR00T_FLAG_W8A8 0x4u      /* with FP8_E4M3 weights: the input rows of every e4m3-weight
                                      GEMM (the DiT's q, k, v, o, MLP and output projections and
@@ -117,8 +122,13 @@ typedef struct gr00t_inputs {
 
 typedef struct gr00t_head gr00t_head;
 
-/* Create a handle for device `device`. Checks the config only; no device memory
- * is allocated until gr00t_finalize. *out is set to NULL on failure. */
+/* Create a handle for device `device`: the engine construction of "Single-GPU inference
+ * for GR00T-N1.7" (Prepare a request and construct the engine), whose batch capacity is
+ * fixed when it is built (max_batch; here also max_vl_len). Checks the config only; no
+ * device memory is allocated until gr00t_finalize. Refuses (E_INVALID_ARG) a capacity for
+ * which a GEMM operand, a cross block's key/value cache or a workspace buffer would exceed
+ * 2^31 - 16 bytes, the range the kernels' 32-bit buffer descriptors address. *out is set
+ * to NULL on failure. */
 int gr00t_create(const gr00t_config* cfg, int device, gr00t_head** out);
 
 /*
@@ -149,11 +159,20 @@ int gr00t_load_weights(gr00t_head* h, const char* name, const void* host_data,
  * one), upload and pack them, allocate the workspace for (max_batch, max_vl_len)
  * and compute the input-independent per-step tables (timestep embedding, adaLN
  * scale/shift of every block and of the output norm, the timestep half of the
- * action encoder's second linear). Synchronous. */
+ * action encoder's second linear): the parts of the engine construction ("Single-GPU
+ * inference for GR00T-N1.7", Prepare a request and construct the engine) that do not
+ * depend on a request; the timestep grid is that of "Model architecture", Inference
+ * (denoising). Synchronous. E_OOM if device memory runs out, E_HIP on a runtime failure. */
 int gr00t_finalize(gr00t_head* h);
 
-/* Capture the K-step hipGraph for batch B and padded VL length L_pad (the analogue
- * of capture profiles). Needs GR00T_FLAG_USE_GRAPH; synchronous. */
+/* Capture the K-step hipGraph for batch B and padded VL length L_pad: the capture
+ * profiles of "Single-GPU inference for GR00T-N1.7" (Prepare a request and construct the
+ * engine), where every served batch shape must match a captured profile. The graph key is
+ * (B, L_pad) alone: the flags are fixed for the handle at create (every graph of a handle
+ * is captured with them), and embodiment ids, masks and noise are data read on the device,
+ * so one graph serves every id mix and mask pattern (the pages' engine also keys on
+ * embodiment categories and mask structures). Needs GR00T_FLAG_USE_GRAPH; synchronous;
+ * preparing a shape twice does nothing. */
 int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len);
 
 /*
@@ -161,8 +180,10 @@ int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len);
  * K Euler steps. Enqueued on `hip_stream` (a hipStream_t; NULL = default stream) and
  * returns without waiting, except in strict mode where the ids are first copied to
  * the host and checked (E_EMBODIMENT). In non-strict mode an out-of-range id is
- * not read: its sample's rows of action_pred are NaN, and the next call on the
- * handle returns E_DEVICE_ERROR once.
+ * not read: its sample's rows of action_pred are NaN, and a later call on the handle
+ * returns E_DEVICE_ERROR once: the first call that finds the copy of the device's
+ * count of invalid ids (taken at the end of every call) completed, so the report is not
+ * lost when calls are enqueued back to back without synchronising.
  */
 int gr00t_get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
                      void* hip_stream);
@@ -204,15 +225,19 @@ int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* acti
                         float* loss, float* v_pred, void* hip_stream);
 
 /* Debug and test entry: the velocity v(x = noise, tau_k) of Euler step `step_k`
- * ([B, H, A] f32, device), without integration or action_mask. inputs.noise must
- * not be NULL. Same stream semantics as gr00t_get_action. */
+ * ([B, H, A] f32, device) that get_action adds, times dt = 1/K, to its Euler state at step
+ * k ("Model architecture", Inference (denoising): the predicted velocity of the denoising
+ * loop), here at x = inputs.noise, without integration or action_mask. With K = 1,
+ * get_action = noise + velocity(step 0). inputs.noise must not be NULL. Same stream
+ * semantics and errors as gr00t_get_action. */
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v,
                    void* hip_stream);
 
 /*
  * The per-row e4m3 quantisation of the W8A8 mode (GR00T_FLAG_W8A8), as its GEMMs apply it
- * to their inputs; the fp8 format is the OCP e4m3fn of the architecture page's fp8 weights
- * (max 448). x: [rows][ld_x] bf16, device, 16-byte aligned; q: [rows][cols] e4m3 codes,
+ * to their inputs. The pages do not name fp8: the e4m3 weight mode serves the high-batch fp8
+ * workload (e4m3 DiT weights with per-output-channel scales), and the format is the OCP
+ * 8-bit floating point specification's E4M3 (no infinities, max 448). x: [rows][ld_x] bf16, device, 16-byte aligned; q: [rows][cols] e4m3 codes,
  * device, 8-byte aligned; scale: [rows] f32, device. For each row r:
  * scale[r] = fp32(max_k |x[r][k]|) / 448 (1 for an all-zero row) and q[r][k] = the e4m3
  * code nearest to the fp32 quotient x[r][k] / scale[r] (ties to the even code, magnitudes
@@ -224,7 +249,9 @@ int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float*
 int gr00t_quantize_e4m3_rows(gr00t_head* h, const void* x, int64_t ld_x, int32_t rows, int32_t cols,
                              uint8_t* q, float* scale, void* hip_stream);
 
-/* Release graphs, device weights and workspace. NULL is a no-op. */
+/* Release graphs, device weights and workspace: "Single-GPU inference for GR00T-N1.7",
+ * Close the engine (releases the graphs and model references). Waits for the handle's
+ * device work to finish first. NULL is a no-op. */
 void gr00t_destroy(gr00t_head* h);
 
 /* Message of the last failure on `h` ("" if none); with h == NULL, the last failure

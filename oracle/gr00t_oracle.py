@@ -34,8 +34,8 @@ H action rows are decoded; the vision-language LayerNorm (vlln) has gain and
 bias; action_mask multiplies the final chunk only. Training forward: the loss is
 the elementwise squared error times action_mask, summed, over the mask's sum plus
 1e-6; the training timestep bucket is floor(t * buckets) in float32. W8A8 mode
-("fp8a8"): the input rows of every e4m3-weight GEMM are quantised to e4m3 per row
-(scale = row amax / 448), the code decided in float32 from the oracle's own value.
+("fp8a8"): the input rows of every e4m3-weight GEMM, the bf16 activations of that mode, are
+quantised to e4m3 per row (scale = row amax / 448), the code decided in float32 from the bf16 value.
 
 Parity: pinned by closed forms and invariants in tests/test_oracle.py; the
 whole network has no printed worked example on the pages, so beyond those pins
@@ -186,9 +186,11 @@ def linear(x, w, b):
 
 def dit_linear(cfg, x, w, b):
     """A linear whose weight is an e4m3 matrix in the fp8 modes (is_fp8_matrix); in the W8A8
-    mode ("fp8a8") its input rows are quantised to e4m3 first (quantize_e4m3_rows)."""
+    mode ("fp8a8") its input rows are quantised to e4m3 first (quantize_e4m3_rows). The rows
+    quantised are the bf16 activations of that mode (bf16 activations, as in the e4m3-weight
+    workload), so the input is rounded to bf16 before its row scale and codes are decided."""
     if cfg["precision"] == "fp8a8":
-        x = quantize_e4m3_rows(x)
+        x = quantize_e4m3_rows(round_bf16(x))
     return linear(x, w, b)
 
 

@@ -5,8 +5,41 @@ import numpy as np
 
 from flow_matching_dit_amd import head as H
 from flow_matching_dit_amd import synth
+from oracle import gr00t_oracle as O
 
 TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "fp8a8": 5e-2}
+# Gate on the displacement action_pred - noise. The stated tolerances apply to action_pred; the
+# displacement error is that error times |ref| / |ref - noise| (about 3.7 at these workloads), so
+# the same figure is a gate about 3.7 times tighter. It holds for the fp32, bf16 and e4m3-weight
+# paths (measured at most 3.4e-3 at full size). The W8A8 mode quantises every GEMM input row to
+# e4m3 (3 mantissa bits): two implementations whose activations differ by rounding take another
+# code on a few percent of the values, and over 32 blocks x 4 steps that gives a displacement
+# error of 5.6e-2 at full size for an action_pred error of 1.5e-2, so W8A8 is gated at twice its
+# action_pred tolerance there.
+TOL_DISP = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "fp8a8": 1e-1}
+
+
+def check_parity(y, ref, noise, action_mask, tol, label, tol_disp=None):
+    """Gate the GPU action_pred against the oracle's: the relative L2 error over every entry and
+    that of every sample on its own below `tol`, and that of the displacement action_pred - noise
+    (the noise passes through exactly and dilutes the first) below `tol_disp` (default `tol`).
+    Masked entries are zero on both sides and are left out of the displacement. Returns the
+    three figures."""
+    tol_disp = tol if tol_disp is None else tol_disp
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nzm = np.asarray(noise, np.float64) * (1.0 if action_mask is None else np.asarray(action_mask, np.float64))
+    err = O.rel_l2(y, ref)
+    disp = O.rel_l2(y - nzm, ref - nzm)
+    per = [O.rel_l2(y[b], ref[b]) for b in range(y.shape[0])]
+    say(f"[parity] {label}: rel_l2 action_pred {err:.3e}, displacement {disp:.3e}, worst sample "
+        f"{max(per):.3e} (of {len(per)})")
+    assert y.shape == ref.shape
+    assert np.all(np.isfinite(y))
+    assert err < tol, (label, "action_pred", err)
+    assert disp < tol_disp, (label, "displacement", disp)
+    assert max(per) < tol, (label, "sample", int(np.argmax(per)), max(per))
+    return err, disp, max(per)
 
 
 def say(*a):

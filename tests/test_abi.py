@@ -209,3 +209,63 @@ def test_canonical_weight_names_are_accepted():
     for name, shape in synth.weight_shapes(w.cfg).items():
         h.load_weight(name, np.zeros(shape, np.float32))
     h.close()
+
+
+def test_binding_checks_dtype_shape_and_device_before_the_call():
+    """The binding refuses tensors the library would misread: an int64 id tensor (read as int32
+    it would give every sample after the first the wrong category), a vl_features of the wrong
+    width or dtype, short buffers, and host tensors. No library call is made (this runs on the
+    CPU, with a handle that was never finalised)."""
+    import torch
+    w = synth.WORKLOADS["tiny_fp32_b1"]
+    h = H.Gr00tHead(w.cfg, max_batch=2, max_vl_len=w.vl_len)
+    try:
+        B, L, c = 2, w.vl_len, w.cfg
+        ok = dict(vl_features=torch.zeros(B, L, c.vl_dim), vl_mask=None, image_mask=None,
+                  state=torch.zeros(B, 1, c.state_dim), embodiment_id=torch.zeros(B, dtype=torch.int32),
+                  noise=torch.zeros(B, c.action_horizon, c.action_dim))
+        bad_cases = [
+            (dict(embodiment_id=torch.zeros(B, dtype=torch.int64)), "embodiment_id has dtype torch.int64"),
+            (dict(vl_features=torch.zeros(B, L, c.vl_dim - 16)), "vl_features has shape"),
+            (dict(vl_features=torch.zeros(B, L, c.vl_dim, dtype=torch.bfloat16)), "vl_features has dtype"),
+            (dict(state=torch.zeros(B, c.state_dim)), "state has shape"),
+            (dict(noise=torch.zeros(B, c.action_horizon, c.action_dim - 1)), "noise has shape"),
+            (dict(vl_mask=torch.zeros(B, L - 1, dtype=torch.uint8)), "vl_mask has shape"),
+            (dict(embodiment_id=torch.zeros(B + 1, dtype=torch.int32)), "embodiment_id has shape"),
+            ({}, "is on cpu"),
+        ]
+        for change, frag in bad_cases:
+            with pytest.raises(ValueError) as e:
+                h.get_action(**{**ok, **change})
+            assert frag in str(e.value), (change.keys(), str(e.value))
+        with pytest.raises(ValueError, match="t has shape"):
+            h.train_forward(ok["vl_features"], None, None, ok["state"], ok["embodiment_id"],
+                            torch.zeros(B, c.action_horizon, c.action_dim), torch.zeros(B + 1), ok["noise"])
+        with pytest.raises(ValueError, match="noise is required"):
+            h.velocity(ok["vl_features"], None, None, ok["state"], ok["embodiment_id"], None, step_k=0)
+        with pytest.raises(ValueError, match="state has dtype"):
+            h.get_action_reuse_vl(B, L, ok["state"].double(), ok["embodiment_id"])
+    finally:
+        h.close()
+
+
+@pytest.mark.parametrize("mb,ml,frag", [
+    (1024, 1024, "VL features"),            # 1024 * 1024 * 2048 * 2 bytes
+    (64, 1 << 20, "VL features"),
+    (1 << 17, 300, "VL features"),
+])
+def test_create_refuses_capacities_past_32_bit_buffer_ranges(mb, ml, frag):
+    """Every GEMM operand, cache layer and workspace buffer is addressed through 32-bit buffer
+    descriptors: a capacity that would need a larger one is refused at create, not computed wrongly."""
+    cfg = synth.WORKLOADS["dit32_bf16_b64"].cfg
+    with pytest.raises(H.Gr00tError) as e:
+        H.Gr00tHead(cfg, max_batch=mb, max_vl_len=ml)
+    assert e.value.status == "E_INVALID_ARG" and "capacity too large" in str(e.value) and frag in str(e.value)
+    # the largest benchmarked capacity is accepted
+    H.Gr00tHead(cfg, max_batch=256, max_vl_len=1024).close()
+
+
+def test_create_refuses_oversized_mlp_width():
+    cfg = replace(synth.WORKLOADS["dit32_bf16_b64"].cfg, ff_dim=1 << 20)
+    with pytest.raises(H.Gr00tError, match="one MLP weight matrix"):
+        H.Gr00tHead(cfg, max_batch=1, max_vl_len=8)

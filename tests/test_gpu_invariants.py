@@ -195,6 +195,41 @@ def test_nonstrict_bad_id_gives_nan_rows_and_deferred_error(wl):
     h.close()
 
 
+def test_deferred_error_survives_pipelined_calls(wl):
+    """A bad-id call followed by clean calls enqueued back to back with no synchronisation:
+    the invalid id is reported exactly once, by whichever later call first finds a completed
+    copy of the device's count (not lost when later calls overwrite the report), and the
+    clean calls' results are unaffected."""
+    import torch
+    w, wt, inp, nz = wl
+    h = build_head(w, wt)
+    bad = dict(inp)
+    bad["embodiment_id"] = inp["embodiment_id"].copy()
+    bad["embodiment_id"][1] = w.cfg.num_categories + 3
+    db = H.device_inputs(bad, nz, h.act_torch_dtype)
+    dg = H.device_inputs(inp, nz, h.act_torch_dtype)
+    yb = h.get_action(**db)          # bad id, not synchronised
+    reports, outs = [], []
+    for _ in range(6):               # clean calls enqueued behind it
+        try:
+            outs.append(h.get_action(**dg))
+        except H.Gr00tError as e:
+            reports.append(e)
+    torch.cuda.synchronize()
+    for _ in range(2):               # after the stream drained: report it now if not yet done
+        try:
+            outs.append(h.get_action(**dg))
+        except H.Gr00tError as e:
+            reports.append(e)
+    torch.cuda.synchronize()
+    assert len(reports) == 1, [str(e) for e in reports]
+    assert reports[0].status == "E_DEVICE_ERROR" and "1 embodiment id" in str(reports[0])
+    assert np.all(np.isnan(yb.cpu().numpy()[1]))
+    ys = [o.cpu().numpy() for o in outs]
+    assert len(ys) == 7 and all(np.array_equal(y, ys[0]) for y in ys) and np.all(np.isfinite(ys[0]))
+    h.close()
+
+
 def test_library_noise_is_standard_normal():
     w = synth.small_variant(synth.WORKLOADS["dit32_bf16_b64"], batch=64, num_layers=2)
     wt, inp = synth.make_weights(w), synth.make_inputs(w)

@@ -8,7 +8,7 @@ import pytest
 
 from flow_matching_dit_amd import head as H
 from flow_matching_dit_amd import synth
-from gpu_util import TOL, build_head, gpu_velocity, say, small
+from gpu_util import TOL, TOL_DISP, build_head, gpu_velocity, say, small
 from oracle import gr00t_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -47,11 +47,13 @@ def test_train_forward_matches_oracle(name, kw):
     h.close()
     ref_loss, ref_vp = O.training_loss(w.cfg.as_dict(), wt, inp, actions, nz, t)
     err = O.rel_l2(vp, ref_vp)
+    per = [O.rel_l2(vp[b], ref_vp[b]) for b in range(w.batch)]
     lerr = abs(loss - ref_loss) / ref_loss
     say(f"[train] {w.name} B={w.batch}: loss {loss:.6f} (oracle {ref_loss:.6f}, rel {lerr:.2e}), "
-        f"v_pred rel_l2 {err:.2e}")
-    tol = TOL[w.cfg.precision]
-    assert err < tol and lerr < tol
+        f"v_pred rel_l2 {err:.2e}, worst sample {max(per):.2e}")
+    # v_pred is a velocity: no noise passes through it, so it is gated like a displacement
+    tol, tol_v = TOL[w.cfg.precision], TOL_DISP[w.cfg.precision]
+    assert lerr < tol and err < tol_v and max(per) < tol_v
 
 
 def test_train_forward_on_the_grid_is_the_inference_velocity():

@@ -481,6 +481,15 @@ def test_row_quantisation_edge_codes():
     assert codes.tolist() == [[0xFE, 0x7E, 0x7E]] and scales[0] == np.float32(3.0) / np.float32(448.0)
 
 
+def test_w8a8_linear_quantises_the_bf16_activation():
+    # the W8A8 GEMM input is the bf16 activation: 1.0625 + 2^-12 rounds to the bf16 value 1.0625,
+    # the midpoint between the e4m3 values 1.0 and 1.125, which goes to the even code (1.0); the
+    # unrounded value lies above the midpoint and would give 1.125
+    x = np.array([[448.0, 1.0625 + 2.0 ** -12, -(1.0625 + 2.0 ** -12)]])
+    y = O.dit_linear({"precision": "fp8a8"}, x, np.eye(3), np.zeros(3))
+    assert y.tolist() == [[448.0, 1.0, -1.0]]
+
+
 def test_w8a8_linear_is_exact_on_representable_operands():
     # inputs and weights on the e4m3 grid with row / column amax 448: both quantisations are the
     # identity, so the fp8a8 linear is the exact product (integer-valued, checked by brute force)

@@ -168,6 +168,12 @@ def _dit_no_output_projection(P, cfg, sa_embs, vl, valid, image, temb):
     return O.ada_layer_norm(P, "out.", h, temb)
 
 
+def _dit_linear_unrounded_a8(cfg, x, w, b):
+    if cfg["precision"] == "fp8a8":
+        x = O.quantize_e4m3_rows(x)
+    return O.linear(x, w, b)
+
+
 CASES = [
     ("gelu", _gelu_tanh, pins.test_gelu_textbook_values),
     ("attention", _attention_no_temperature, pins.test_attention_temperature),
@@ -195,6 +201,7 @@ CASES = [
     ("action_decoder", _action_decoder_no_relu, pins.test_action_decoder_relu_between_linears),
     ("dit", _dit_plain_final_norm, pins.test_dit_output_head_is_modulated_norm_then_projection),
     ("dit", _dit_no_output_projection, pins.test_dit_output_head_is_modulated_norm_then_projection),
+    ("dit_linear", _dit_linear_unrounded_a8, pins.test_w8a8_linear_quantises_the_bf16_activation),
 ]
 
 

@@ -149,13 +149,19 @@ struct gr00t_head {
   // reported once by the next call that finds such a completed copy.
   static constexpr int kReportSlots = 4;
   struct ReportSlot {
-    uint8_t* host = nullptr;  // [4 bytes count][max_batch flags]
+    uint8_t* host = nullptr;  // [4 bytes invalid-id count][4 bytes block-kernel timeouts][max_batch flags]
     hipEvent_t ev = nullptr;
     bool recorded = false;
     int B = 0;
   } rep[kReportSlots];
   int rep_next = 0;
   uint32_t bad_reported = 0;
+  // persistent kernel for the DiT blocks at B = 1 (persist.hip): usable for this model and
+  // device, its scratch, the per-block weight table, and the timeouts already reported
+  bool persist_ok = false;
+  void* persist_base = nullptr;
+  PBlock* persist_blocks = nullptr;
+  uint32_t persist_err_reported = 0;
   // (B, L_pad) of the VL key/value caches and key masks in the workspace: those of the last
   // call that ran the full prologue (0, 0: none yet)
   int kv_B = 0, kv_L = 0;
@@ -218,7 +224,8 @@ int check_config(const gr00t_config* c, std::string& why) {
   if (!(c->act_dtype == GR00T_F32 || c->act_dtype == GR00T_BF16)) return bad("act_dtype must be F32 or BF16");
   if ((c->weight_dtype == GR00T_F32) != (c->act_dtype == GR00T_F32))
     return bad("F32 weights go with F32 activations, BF16/FP8 weights with BF16 activations");
-  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8)) return bad("unknown flag bits");
+  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8 | GR00T_FLAG_PERSIST))
+    return bad("unknown flag bits");
   if ((c->flags & GR00T_FLAG_W8A8) && c->weight_dtype != GR00T_FP8_E4M3)
     return bad("GR00T_FLAG_W8A8 needs FP8_E4M3 weights");
   // The kernels address each GEMM operand, cache layer and workspace buffer through a 32-bit
@@ -469,11 +476,12 @@ void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
 
 enum KClass {
   K_VLLN = 0, K_KV_PROJ, K_STATE_ENC, K_ACTION_ENC, K_ADALN, K_QKV_PROJ, K_Q_PROJ, K_ATTN_SELF, K_ATTN_CROSS,
-  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_GRAPH, K_NCLASS
+  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_GRAPH, K_BLOCKS, K_NCLASS
 };
 const char* const kClassNames[K_NCLASS] = {"vlln", "kv_proj", "state_enc", "action_enc", "adaln", "qkv_proj",
                                            "q_proj", "attn_self", "attn_cross", "o_proj", "norm3", "ff_up",
-                                           "ff_down", "out_proj", "decoder", "small", "steps_graph"};
+                                           "ff_down", "out_proj", "decoder", "small", "steps_graph",
+                                           "blocks_b1"};
 
 // Returns the index of the start event recorded on s, or -1 when not profiling.
 int prof_begin(gr00t_head* h, hipStream_t s) {
@@ -713,6 +721,59 @@ int build_sample_tables(gr00t_head* h, const float* t, int B, hipStream_t s) {
   return GR00T_OK;
 }
 
+// ------------------------------------------------------------------ persistent B = 1 blocks
+
+unsigned* persist_err(gr00t_head* h) {
+  PersistArgs pa{};
+  persist_bind_scratch(pa, h->persist_base);
+  return persist_error_word(pa);
+}
+
+// Whether this call's DiT blocks run in the persistent kernel: one sample, bf16 weights and
+// activations, the kernel's model widths, and the step graph key's VL length.
+bool use_persist(const gr00t_head* h, int B, int L, bool per_sample) {
+  const gr00t_config& c = h->cfg;
+  return h->persist_ok && B == 1 && !per_sample &&
+         persist_b1_fits(c.hidden, c.ff_dim, c.num_heads, c.head_dim, c.action_horizon + 1, L, 256);
+}
+
+// Set up the persistent kernel at finalize when the caller asks for it and the model and the
+// device allow it.
+int persist_setup(gr00t_head* h) {
+  const gr00t_config& c = h->cfg;
+  int cus = 0;
+  HIPCHK(h, hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device));
+  if (!(c.flags & GR00T_FLAG_PERSIST) || c.weight_dtype != GR00T_BF16 || c.act_dtype != GR00T_BF16 ||
+      !persist_b1_fits(c.hidden, c.ff_dim, c.num_heads, c.head_dim, c.action_horizon + 1, 1, cus))
+    return GR00T_OK;
+  HIPCHK(h, persist_init());
+  const size_t tab = (size_t)c.num_layers * sizeof(PBlock);
+  if (hipMalloc(&h->persist_base, persist_scratch_bytes() + tab) != hipSuccess) {
+    h->persist_base = nullptr;
+    (void)hipGetLastError();
+    return fail(h, GR00T_E_OOM, "persistent kernel scratch: device allocation failed");
+  }
+  HIPCHK(h, hipMemset(h->persist_base, 0, persist_scratch_bytes()));
+  h->persist_blocks = (PBlock*)((char*)h->persist_base + persist_scratch_bytes());
+  std::vector<PBlock> blocks(c.num_layers);
+  for (int l = 0; l < c.num_layers; ++l) {
+    const LayerOff& lo = h->lay.L[l];
+    PBlock& b = blocks[l];
+    b.wq = at<uint16_t>(h, lo.wq);
+    b.bq = at<float>(h, lo.bq);
+    b.wo = at<uint16_t>(h, lo.wo);
+    b.bo = at<float>(h, lo.bo);
+    b.w1 = at<uint16_t>(h, lo.w1);
+    b.b1 = at<float>(h, lo.b1);
+    b.w2 = at<uint16_t>(h, lo.w2);
+    b.b2 = at<float>(h, lo.b2);
+    b.nq = (l % 2) == 1 ? 3 : 1;
+  }
+  HIPCHK(h, hipMemcpy(h->persist_blocks, blocks.data(), tab, hipMemcpyHostToDevice));
+  h->persist_ok = true;
+  return GR00T_OK;
+}
+
 // ------------------------------------------------------------------ the launch sequence
 
 // reuse_vl: the VL part (key masks, VL LayerNorm, K/V projection) is skipped and the caches
@@ -875,7 +936,24 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
     };
     int pend = 0;  // partial sums not yet added to h
     const long pstride = M * D;
-    for (int l = 0; l < Nl; ++l) {
+    if (use_persist(h, B, L, per_sample)) {
+      PersistArgs pa{};
+      persist_bind_scratch(pa, h->persist_base);
+      pa.blocks = h->persist_blocks;
+      pa.nl = Nl;
+      pa.S = S;
+      pa.h = h->w.h;
+      pa.ada = ada_of(0);
+      pa.kc = (const uint16_t*)h->w.kc;
+      pa.vc = (const uint16_t*)h->w.vc;
+      pa.Lp = round32(L);
+      pa.kv_layer = (long)pa.Lp * D;
+      pa.code = h->w.code;
+      pa.L = L;
+      pa.text_every = c.attend_text_every_n_blocks;
+      LAUNCH(h, s, K_BLOCKS, launch_dit_b1_persist(pa, s));
+    }
+    for (int l = 0; l < Nl && !use_persist(h, B, L, per_sample); ++l) {
       const LayerOff& lo = lay.L[l];
       const bool self = (l % 2) == 1;
       LAUNCH(h, s, K_ADALN, launch_resid_layernorm(h->w.h, h->w.part, pend, pstride, ny, nt, (int)M, D, ada_of(l), s,
@@ -1017,20 +1095,29 @@ int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out, bool re
 
 // Strict-mode id check on the host, and the deferred report of bad ids seen on the device.
 int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
-  uint32_t newest = h->bad_reported;
+  uint32_t newest = h->bad_reported, perr = h->persist_err_reported;
   int sample = -1;
   for (auto& r : h->rep) {
     if (!r.recorded || hipEventQuery(r.ev) != hipSuccess) continue;
-    uint32_t cnt;
+    uint32_t cnt, pe;
     std::memcpy(&cnt, r.host, 4);
+    std::memcpy(&pe, r.host + 4, 4);
+    if ((int32_t)(pe - perr) > 0) perr = pe;
     if ((int32_t)(cnt - newest) > 0) {
       newest = cnt;
       sample = -1;
       for (int b = 0; b < r.B && sample < 0; ++b)
-        if (r.host[4 + b]) sample = b;
+        if (r.host[8 + b]) sample = b;
     }
   }
   (void)hipGetLastError();  // a not-ready query leaves no error behind
+  if (perr != h->persist_err_reported) {
+    h->persist_err_reported = perr;
+    h->persist_ok = false;  // later calls take the launch-per-step path
+    return fail(h, GR00T_E_DEVICE_ERROR,
+                "an earlier call's persistent block kernel gave up (its workgroups were not all resident at once, or not "
+                "32 on each XCD); its result is invalid, and the handle now launches the blocks step by step");
+  }
   if (newest != h->bad_reported) {
     const uint32_t n = newest - h->bad_reported;
     h->bad_reported = newest;
@@ -1056,7 +1143,8 @@ int enqueue_report(gr00t_head* h, int B, hipStream_t s) {
   auto& r = h->rep[h->rep_next];
   h->rep_next = (h->rep_next + 1) % gr00t_head::kReportSlots;
   HIPCHK(h, hipMemcpyAsync(r.host, h->w.bad_count, 4, hipMemcpyDeviceToHost, s));
-  HIPCHK(h, hipMemcpyAsync(r.host + 4, h->w.bad, B, hipMemcpyDeviceToHost, s));
+  if (h->persist_ok) HIPCHK(h, hipMemcpyAsync(r.host + 4, persist_err(h), 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(h, hipMemcpyAsync(r.host + 8, h->w.bad, B, hipMemcpyDeviceToHost, s));
   HIPCHK(h, hipEventRecord(r.ev, s));
   r.recorded = true;
   r.B = B;
@@ -1209,10 +1297,13 @@ int gr00t_finalize(gr00t_head* h) {
   HIPCHK(h, hipMemset(h->w.v, 0, Bm * Sp * D * ab));
   HIPCHK(h, hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
   for (auto& r : h->rep) {
-    HIPCHK(h, hipHostMalloc((void**)&r.host, 4 + Bm, hipHostMallocDefault));
+    HIPCHK(h, hipHostMalloc((void**)&r.host, 8 + Bm, hipHostMallocDefault));
+    std::memset(r.host, 0, 8 + Bm);
     HIPCHK(h, hipEventCreateWithFlags(&r.ev, hipEventDisableTiming));
   }
-  int rc = build_tables(h, h->cap_stream);
+  int rc = persist_setup(h);
+  if (rc != GR00T_OK) return rc;
+  rc = build_tables(h, h->cap_stream);
   if (rc != GR00T_OK) return rc;
   HIPCHK(h, hipStreamSynchronize(h->cap_stream));
   h->finalized = true;
@@ -1364,6 +1455,7 @@ void gr00t_destroy(gr00t_head* h) {
   }
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   if (h->tr_base) (void)hipFree(h->tr_base);
+  if (h->persist_base) (void)hipFree(h->persist_base);
   if (h->arena || h->wsbase) (void)hipDeviceSynchronize();
   if (h->arena) (void)hipFree(h->arena);
   if (h->wsbase) (void)hipFree(h->wsbase);

@@ -170,4 +170,51 @@ hipError_t launch_silu(const float* x, float* y, long n, hipStream_t s);
 // fp32 -> act dtype copy of n elements.
 hipError_t launch_convert(const float* x, void* y, DType yt, long n, hipStream_t s);
 
+// ------------------------------------------------------------------ persistent B = 1 blocks
+// Weights of one DiT block as the persistent kernel reads them (packed [out][in] bf16).
+struct PBlock {
+  const uint16_t* wq;  // [nq * D][D]: q (cross blocks, nq = 1) or q; k; v (self blocks, nq = 3)
+  const float* bq;     // [nq * D]
+  const uint16_t* wo;  // [D][D]
+  const float* bo;     // [D]
+  const uint16_t* w1;  // [F][D]
+  const float* b1;     // [F]
+  const uint16_t* w2;  // [D][F]
+  const float* b2;     // [D]
+  int nq;
+};
+
+// One Euler step's DiT blocks for one sample in one launch (persist.hip): D = 1536 (32 heads
+// of 48), F = 6144, S <= 32 rows, on a device of 256 CUs in 8 XCDs.
+struct PersistArgs {
+  const PBlock* blocks;  // [nl] (device)
+  int nl;
+  int S;                 // rows: the state token and H action tokens
+  float* h;              // [S][D] fp32 residual stream: the blocks' input, replaced by their output
+  const float* ada;      // [nl][2D] adaLN [scale | shift] of every block at this step
+  const uint16_t* kc;    // key cache of the cross blocks [cross block][head][Lp][hd] (B = 1)
+  const uint16_t* vc;    // value cache [cross block][head][Lp / 32][hd][32]
+  long kv_layer;         // elements between two cross blocks' caches
+  const uint8_t* code;   // [L] key mask codes: bit 0 text blocks, bit 1 image blocks
+  int L, Lp, text_every;
+  // scratch (persist_scratch_bytes, bound by persist_bind_scratch)
+  float* hx;
+  uint16_t* qkvx;
+  uint16_t* ox;
+  uint16_t* ux;
+  float* part;
+  float2* statx;
+  unsigned* ctl;
+};
+// Whether the persistent kernel serves this shape (model widths, rows, VL length, CU count).
+bool persist_b1_fits(int D, int F, int nh, int hd, int S, int L, int num_cus);
+size_t persist_scratch_bytes();
+void persist_bind_scratch(PersistArgs& a, void* base);
+// device word counting the persistent kernel's timed-out waits (never cleared)
+unsigned* persist_error_word(const PersistArgs& a);
+// allows the kernel its dynamic LDS (once per process, before the first launch)
+hipError_t persist_init();
+// clears the control words, then launches the kernel (two launches on s)
+hipError_t launch_dit_b1_persist(const PersistArgs& a, hipStream_t s);
+
 }  // namespace gr00t

@@ -19,6 +19,7 @@ F32, BF16, FP8_E4M3, U8, I32 = 0, 1, 2, 3, 4
 FLAG_STRICT = 0x1
 FLAG_USE_GRAPH = 0x2
 FLAG_W8A8 = 0x4
+FLAG_PERSIST = 0x8
 
 STATUS = {
     0: "OK", -1: "E_INVALID_ARG", -2: "E_SHAPE", -3: "E_EMBODIMENT", -4: "E_NOT_FINALIZED",

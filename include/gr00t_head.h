@@ -71,6 +71,16 @@ typedef enum gr00t_dtype {
                                      at create. Adds K + 4 bytes per row of the largest such
                                      GEMM input to the workspace. */
 
+#define GR00T_FLAG_PERSIST 0x8u /* run the DiT blocks of a one-sample call (bf16, hidden 1536,
+                                   32 heads of 48, MLP 6144, at most 32 tokens) in one persistent
+                                   kernel per Euler step, one workgroup per compute unit that
+                                   streams each block's weights while it waits for the others,
+                                   instead of one launch per step of the block. The kernel needs
+                                   all 256 compute units to itself: a wait that does not end
+                                   within its bound gives up, the call's result is then wrong,
+                                   the next call reports GR00T_E_DEVICE and the handle falls back
+                                   to the launch-per-step path. Ignored where it does not apply. */
+
 /*
  * Model and capacity. Widths follow the "Model configuration" table of the
  * architecture page: hidden = num_heads * head_dim is used for the state and

@@ -14,7 +14,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libgr00t_head.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemm.hip", "ops.hip", "persist.hip", "head.cpp"]
+SOURCES = ["gemm.hip", "ops.hip", "persist.hip", "scratch.hip", "head.cpp"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 # Packed-fp32 VALU forms are kept out of the device code.

@@ -171,6 +171,9 @@ struct gr00t_head {
           *c2 = nullptr;
   } tr;
   void* tr_base = nullptr;
+  // device address of the library's fixed scratch area on this handle's device (scratch.hip),
+  // looked up at finalize: the per-sample tables of gr00t_train_forward_noalloc
+  void* static_scratch = nullptr;
   std::vector<int> tau;
   // launch timing (gr00t_profile_*)
   bool prof_on = false;
@@ -658,39 +661,47 @@ int build_tables(gr00t_head* h, hipStream_t s) {
   return GR00T_OK;
 }
 
+// Bytes of the per-sample tables of the training forward for `rows` samples: the sinusoid of
+// t, tau's embedding, the two timestep-encoder activations, SiLU(temb), the category term of
+// the action encoder and every block's adaLN [scale | shift], each 256-byte aligned.
+size_t sample_tables_bytes(const gr00t_config& c, size_t rows) {
+  const size_t n[7] = {rows * c.time_freq_dim, rows * c.hidden, rows * c.hidden, rows * c.hidden,
+                       rows * c.hidden, rows * c.hidden, rows * (size_t)(c.num_layers + 1) * 2 * c.hidden};
+  size_t b = 0;
+  for (size_t k : n) b += (k * sizeof(float) + 255) & ~(size_t)255;
+  return b;
+}
+
 // Per-sample timestep tables of the training forward ("GR00T model class", Flow matching
 // diffusion, Training): the bucket floor(t_b * buckets) of each sample, its timestep
 // embedding, the adaLN [scale | shift] of every block and of the output norm, and the
 // timestep term of the action encoder's second linear under the sample's category. The
 // GEMM sequence is that of build_tables with one row per sample instead of one per step.
-int build_sample_tables(gr00t_head* h, const float* t, int B, hipStream_t s) {
+// The tables go to `base` laid out for `rows` samples (every table fully written, nothing
+// accumulated), or, with base NULL, to the handle's own allocation.
+int build_sample_tables(gr00t_head* h, const float* t, int B, hipStream_t s, void* base = nullptr, int rows = 0) {
   const gr00t_config& c = h->cfg;
   const int D = c.hidden, Nl = c.num_layers, T = c.time_freq_dim;
   const Layout& L = h->lay;
   const DType mw = c.weight_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
-  if (!h->tr_base) {
-    const size_t Bm = c.max_batch;
-    const size_t n_sin = Bm * T, n_d = Bm * D, n_ada = Bm * (size_t)(Nl + 1) * 2 * D;
-    const size_t total = n_sin + 5 * n_d + n_ada;
-    if (hipMalloc(&h->tr_base, total * sizeof(float)) != hipSuccess) {
-      h->tr_base = nullptr;
-      (void)hipGetLastError();
-      return fail(h, GR00T_E_OOM, "training tables: device allocation failed");
+  if (!base) {  // the handle's own tables, sized for max_batch, allocated on the first call
+    if (!h->tr_base) {
+      if (hipMalloc(&h->tr_base, sample_tables_bytes(c, c.max_batch)) != hipSuccess) {
+        h->tr_base = nullptr;
+        (void)hipGetLastError();
+        return fail(h, GR00T_E_OOM, "training tables: device allocation failed");
+      }
     }
-    float* p = (float*)h->tr_base;
-    h->tr.sin_t = p;
-    p += n_sin;
-    h->tr.tauemb = p;
-    p += n_d;
-    h->tr.t1 = p;
-    p += n_d;
-    h->tr.temb = p;
-    p += n_d;
-    h->tr.stemb = p;
-    p += n_d;
-    h->tr.c2 = p;
-    p += n_d;
-    h->tr.ada = p;
+    base = h->tr_base;
+    rows = c.max_batch;
+  }
+  const size_t n[7] = {(size_t)rows * T, (size_t)rows * D, (size_t)rows * D, (size_t)rows * D, (size_t)rows * D,
+                       (size_t)rows * D, (size_t)rows * (Nl + 1) * 2 * D};
+  float** dst[7] = {&h->tr.sin_t, &h->tr.tauemb, &h->tr.t1, &h->tr.temb, &h->tr.stemb, &h->tr.c2, &h->tr.ada};
+  char* p = (char*)base;
+  for (int i = 0; i < 7; ++i) {
+    *dst[i] = (float*)p;
+    p += (n[i] * sizeof(float) + 255) & ~(size_t)255;
   }
   HIPCHK(h, launch_sinusoid_t(t, B, c.num_timestep_buckets, T, h->tr.sin_t, s));
   HIPCHK(h, launch_sinusoid_t(t, B, c.num_timestep_buckets, D, h->tr.tauemb, s));
@@ -1153,6 +1164,44 @@ int enqueue_report(gr00t_head* h, int B, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+int train_forward(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t, float* loss,
+                  float* v_pred, void* hip_stream, bool no_alloc) {
+  int rc = check_inputs(h, in, loss);
+  if (rc != GR00T_OK) return rc;
+  if (!actions || !t) return fail(h, GR00T_E_INVALID_ARG, "actions and t are required");
+  if (!in->noise) return fail(h, GR00T_E_INVALID_ARG, "the training forward needs inputs.noise");
+  const gr00t_config& c = h->cfg;
+  const int B = in->batch, per = c.action_horizon * c.action_dim;
+  if (no_alloc) {
+    const size_t need = sample_tables_bytes(c, B);
+    if (need > static_scratch_bytes())
+      return fail(h, GR00T_E_SHAPE,
+                  "gr00t_train_forward_noalloc: " + std::to_string(B) + " samples need " + std::to_string(need) +
+                      " bytes of per-sample tables; the fixed scratch area holds " +
+                      std::to_string(static_scratch_bytes()) + " (" +
+                      std::to_string(static_scratch_bytes() / sample_tables_bytes(c, 1)) + " samples of this model)");
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  HIPCHK(h, hipSetDevice(h->device));
+  rc = pre_call_checks(h, in, s);
+  if (rc != GR00T_OK) return rc;
+  rc = run_prologue(h, in, s);  // VL, ids, state token (its x = noise is replaced below)
+  if (rc != GR00T_OK) return rc;
+  rc = no_alloc ? build_sample_tables(h, t, B, s, h->static_scratch, B) : build_sample_tables(h, t, B, s);
+  if (rc != GR00T_OK) return rc;
+  LAUNCH(h, s, K_SMALL, launch_flow_interp(actions, in->noise, t, h->w.x, B, per, s));
+  rc = run_steps(h, B, in->vl_len, 0, 1, false, s, true);
+  if (rc != GR00T_OK) return rc;
+  LAUNCH(h, s, K_SMALL, launch_masked_mse(h->w.vout, actions, in->noise, in->action_mask, h->w.bad, B, per, loss, s));
+  if (v_pred) HIPCHK(h, hipMemcpyAsync(v_pred, h->w.vout, sizeof(float) * B * per, hipMemcpyDeviceToDevice, s));
+  rc = enqueue_report(h, B, s);
+  if (rc != GR00T_OK) return rc;
+  h->calls++;
+  return GR00T_OK;
+}
+}  // namespace
+
 // ====================================================================== C ABI
 
 extern "C" {
@@ -1301,6 +1350,7 @@ int gr00t_finalize(gr00t_head* h) {
     std::memset(r.host, 0, 8 + Bm);
     HIPCHK(h, hipEventCreateWithFlags(&r.ev, hipEventDisableTiming));
   }
+  HIPCHK(h, static_scratch_address(h->device, &h->static_scratch));
   int rc = persist_setup(h);
   if (rc != GR00T_OK) return rc;
   rc = build_tables(h, h->cap_stream);
@@ -1376,31 +1426,15 @@ int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* acti
   return get_action(h, in, action_pred, hip_stream, true);
 }
 
+
 int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t, float* loss,
                         float* v_pred, void* hip_stream) {
-  int rc = check_inputs(h, in, loss);
-  if (rc != GR00T_OK) return rc;
-  if (!actions || !t) return fail(h, GR00T_E_INVALID_ARG, "actions and t are required");
-  if (!in->noise) return fail(h, GR00T_E_INVALID_ARG, "the training forward needs inputs.noise");
-  const gr00t_config& c = h->cfg;
-  const int B = in->batch, per = c.action_horizon * c.action_dim;
-  hipStream_t s = (hipStream_t)hip_stream;
-  HIPCHK(h, hipSetDevice(h->device));
-  rc = pre_call_checks(h, in, s);
-  if (rc != GR00T_OK) return rc;
-  rc = run_prologue(h, in, s);  // VL, ids, state token (its x = noise is replaced below)
-  if (rc != GR00T_OK) return rc;
-  rc = build_sample_tables(h, t, B, s);
-  if (rc != GR00T_OK) return rc;
-  LAUNCH(h, s, K_SMALL, launch_flow_interp(actions, in->noise, t, h->w.x, B, per, s));
-  rc = run_steps(h, B, in->vl_len, 0, 1, false, s, true);
-  if (rc != GR00T_OK) return rc;
-  LAUNCH(h, s, K_SMALL, launch_masked_mse(h->w.vout, actions, in->noise, in->action_mask, h->w.bad, B, per, loss, s));
-  if (v_pred) HIPCHK(h, hipMemcpyAsync(v_pred, h->w.vout, sizeof(float) * B * per, hipMemcpyDeviceToDevice, s));
-  rc = enqueue_report(h, B, s);
-  if (rc != GR00T_OK) return rc;
-  h->calls++;
-  return GR00T_OK;
+  return train_forward(h, in, actions, t, loss, v_pred, hip_stream, false);
+}
+
+int gr00t_train_forward_noalloc(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t,
+                                float* loss, float* v_pred, void* hip_stream) {
+  return train_forward(h, in, actions, t, loss, v_pred, hip_stream, true);
 }
 
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v, void* hip_stream) {

@@ -214,6 +214,9 @@ void persist_bind_scratch(PersistArgs& a, void* base);
 unsigned* persist_error_word(const PersistArgs& a);
 // allows the kernel its dynamic LDS (once per process, before the first launch)
 hipError_t persist_init();
+// scratch.hip: the fixed device scratch area of the entry points that do not allocate
+size_t static_scratch_bytes();
+hipError_t static_scratch_address(int device, void** ptr);  // `device` must be current
 // clears the control words, then launches the kernel (two launches on s)
 hipError_t launch_dit_b1_persist(const PersistArgs& a, hipStream_t s);
 

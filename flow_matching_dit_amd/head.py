@@ -30,7 +30,8 @@ STATUS = {
 
 # Every exported symbol of include/gr00t_head.h.
 EXPORTS = ("gr00t_create", "gr00t_load_weights", "gr00t_finalize", "gr00t_prepare", "gr00t_get_action",
-           "gr00t_get_action_reuse_vl", "gr00t_train_forward", "gr00t_velocity", "gr00t_quantize_e4m3_rows",
+           "gr00t_get_action_reuse_vl", "gr00t_train_forward", "gr00t_train_forward_noalloc", "gr00t_velocity",
+           "gr00t_quantize_e4m3_rows",
            "gr00t_destroy",
            "gr00t_last_error", "gr00t_device_bytes", "gr00t_profile_enable", "gr00t_profile_read",
            "gr00t_profile_class_name")
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gr00t_get_action_reuse_vl.restype = c_int
     lib.gr00t_train_forward.argtypes = [c_void_p, POINTER(Gr00tInputs), c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p]
+    lib.gr00t_train_forward_noalloc.argtypes = lib.gr00t_train_forward.argtypes
+    lib.gr00t_train_forward_noalloc.restype = c_int
     lib.gr00t_train_forward.restype = c_int
     lib.gr00t_velocity.argtypes = [c_void_p, POINTER(Gr00tInputs), c_int32, c_void_p, c_void_p]
     lib.gr00t_velocity.restype = c_int
@@ -282,6 +285,25 @@ class Gr00tHead:
         self._check(self.lib.gr00t_train_forward(self.h, ctypes.byref(inp), _ptr(actions), _ptr(t),
                                                  c_void_p(loss.data_ptr()), _ptr(vp), self._stream(stream)))
         return loss, vp
+
+    def train_forward_noalloc(self, vl_features, vl_mask, image_mask, state, embodiment_id, actions, t, noise,
+                              loss, v_pred=None, action_mask=None, stream=None):
+        """The training forward into caller-provided outputs (loss [1] f32, optional v_pred
+        [B, H, A] f32, both on the handle's device) through the entry point that allocates
+        nothing: its per-sample tables live in the library's fixed scratch area."""
+        import torch
+        B = int(vl_features.shape[0])
+        for dev in (None, self.torch_device):
+            _expect("actions", actions, (B, self._c.action_horizon, self._c.action_dim), (torch.float32,), dev)
+            _expect("t", t, (B,), (torch.float32,), dev)
+            _expect("loss", loss, (1,), (torch.float32,), dev)
+            _expect("v_pred", v_pred, (B, self._c.action_horizon, self._c.action_dim), (torch.float32,), dev,
+                    optional=True)
+        inp = self._inputs(vl_features, vl_mask, image_mask, state, embodiment_id, noise, action_mask, None,
+                           need_noise=True)
+        self._check(self.lib.gr00t_train_forward_noalloc(self.h, ctypes.byref(inp), _ptr(actions), _ptr(t),
+                                                         _ptr(loss), _ptr(v_pred), self._stream(stream)))
+        return loss, v_pred
 
     def velocity(self, vl_features, vl_mask, image_mask, state, embodiment_id, noise, step_k: int,
                  stream=None):

@@ -226,13 +226,28 @@ int gr00t_get_action_reuse_vl(gr00t_head* h, const gr00t_inputs* in, float* acti
  * actions [B, H, A] f32, loss [1] f32 and the optional v_pred [B, H, A] f32 are device
  * pointers. Forward only (no gradients). Enqueued on `hip_stream` like gr00t_get_action,
  * not captured in a graph; the first call allocates the per-sample tables
- * (max_batch * ((num_layers + 1) * 2 * hidden + 6 * hidden + time_freq_dim) floats, freed by
+ * (max_batch * ((num_layers + 1) * 2 * hidden + 5 * hidden + time_freq_dim) floats, freed by
  * gr00t_destroy). Errors as gr00t_get_action, E_INVALID_ARG without actions, t or
  * inputs.noise, E_OOM if the tables cannot be allocated. In non-strict mode an invalid id
  * makes the loss NaN.
  */
 int gr00t_train_forward(gr00t_head* h, const gr00t_inputs* in, const float* actions, const float* t,
                         float* loss, float* v_pred, void* hip_stream);
+
+/* gr00t_train_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, but the per-sample tables, which gr00t_train_forward allocates on
+ * its first call, go to a fixed scratch area of 32 MiB that the library holds on every
+ * device it runs on until the process ends. The call allocates nothing (with launch timing
+ * off). Limit: batch * ((num_layers + 1) * 2 * hidden + 5 * hidden + time_freq_dim) floats,
+ * each of the seven tables rounded up to 256 bytes, at most 32 MiB (76 samples of the
+ * 32-block model, hidden 1536); larger batches are refused with GR00T_E_SHAPE before
+ * anything is enqueued. Every handle on a device shares that device's area and each call
+ * overwrites it (nothing in it needs to start at zero): calls that overlap on one device,
+ * on different streams or from different threads, race. Other arguments, semantics and
+ * errors as gr00t_train_forward. */
+int gr00t_train_forward_noalloc(gr00t_head* h, const gr00t_inputs* in, const float* actions,
+                                const float* t, float* loss, float* v_pred, void* hip_stream);
 
 /* Debug and test entry: the velocity v(x = noise, tau_k) of Euler step `step_k`
  * ([B, H, A] f32, device) that get_action adds, times dt = 1/K, to its Euler state at step

@@ -13,7 +13,12 @@ database of the same command (rocpd SQLite):
   bandwidth  HBM bytes per dispatch (calibrated FETCH_SIZE + WRITE_SIZE) over the traced
              duration, against the 8 TB/s peak
 
+The kernel-only average duration of a class's kernel comes from the same database:
+  trace      average duration and launch count of the kernels whose name contains S
+
 usage:
+  python -m flow_matching_dit_amd.measure trace --kernel-substr S --cls C --workload W \
+      --db results.db --command "..." --out profiles/trace_C_W.json
   python -m flow_matching_dit_amd.measure traffic --kernel-substr S --cls C --workload W \
       --fetch fetch.csv --write write.csv --calib-fetch cf.csv --calib-write cw.csv \
       --calib-bytes N --out profiles/traffic_C_W.json
@@ -144,6 +149,21 @@ def bandwidth(args):
               f"{100.0 * gbs / HBM_PEAK_GBS:.1f}% |")
 
 
+def trace(args):
+    import sqlite3
+    db = sqlite3.connect(args.db)
+    rows = db.execute("select name, count(*), avg(duration) from kernels group by name").fetchall()
+    hits = [(n, c, d) for n, c, d in rows if args.kernel_substr in n]
+    if len(hits) != 1:
+        sys.exit(f"{len(hits)} kernel names contain {args.kernel_substr!r}; need exactly one")
+    name, n, avg_ns = hits[0]
+    res = {"class": args.cls, "workload": args.workload, "kernel": name, "launches": n,
+           "avg_us": avg_ns / 1e3, "command": args.command, "kernel_source_hash": kernel_source_hash()}
+    with open(args.out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -162,6 +182,9 @@ def main():
     b.add_argument("--calib-bytes", type=int, required=True)
     b.add_argument("--calib-substr", default="copy")
     b.add_argument("--substr", default="gemm")
+    tr = sub.add_parser("trace")
+    for k in ("kernel-substr", "cls", "workload", "db", "command", "out"):
+        tr.add_argument("--" + k, required=True)
     sub.add_parser("hash")
     args = ap.parse_args()
     if args.cmd == "traffic":
@@ -170,6 +193,8 @@ def main():
         mfma(args)
     elif args.cmd == "bandwidth":
         bandwidth(args)
+    elif args.cmd == "trace":
+        trace(args)
     else:
         print(kernel_source_hash())
 

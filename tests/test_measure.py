@@ -90,3 +90,17 @@ def test_kernel_source_hash_is_stable():
     h = measure.kernel_source_hash()
     assert len(h) == 16 and h == measure.kernel_source_hash()
     int(h, 16)
+
+
+def test_trace_averages_the_one_matching_kernel(tmp_path):
+    import json
+    db = _trace(tmp_path / "t.db", [(K1, 30000), (K1, 32000), (K2, 5000)])
+    out = tmp_path / "trace.json"
+    args = SimpleNamespace(db=db, kernel_substr="gemm_dma_kernel<256, 128", cls="ff_up", workload="w",
+                           command="rocprofv3 ...", out=str(out))
+    measure.trace(args)
+    r = json.loads(out.read_text())
+    assert r["launches"] == 2 and abs(r["avg_us"] - 31.0) < 1e-9 and r["kernel"] == K1
+    assert r["kernel_source_hash"] == measure.kernel_source_hash()
+    with pytest.raises(SystemExit):   # no kernel, or more than one, matches
+        measure.trace(SimpleNamespace(**dict(vars(args), kernel_substr="gr00t::")))

@@ -266,7 +266,7 @@ template <int BM, int BN, int WM, int WN, int EK>
 __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
                                               const floatx4_t (&acc)[BM / WM / 16][BN / WN / 16], int g, int cat,
                                               int split, int r0, int n0, int wm, int wn, int lane,
-                                              const float4* res = nullptr) {
+                                              const float4* res = nullptr, int bfirst = 0, int brows = 1) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   const bool add_bias = (EK != EPI_PARTIAL) || split == 0;
@@ -350,6 +350,8 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& a, const Epi& e,
             const float4 o = res[i * FN + j];
             *(float4*)((float*)e.out + ((long)g * e.out_gstride + e.out_row_off + r) * e.out_ld + n) =
                 make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+          } else if (a.chunks) {  // category bucket: row r % brows of sample perm[first + r / brows]
+            epi_store<EK, 4>(e, a.perm[bfirst + r / brows], r % brows, n, v, cat, split);
           } else {
             epi_store<EK, 4>(e, g, r, n, v, cat, split);
           }
@@ -485,14 +487,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
     split = blockIdx.z;
   }
   const int g = blockIdx.y;
-  const int cat = a.ids ? a.ids[g] : 0;
+  int cat = a.ids ? a.ids[g] : 0;
   const int r0 = tm * BM, n0 = tn * BN;
   const int kbeg = split * a.k_per_split;
   const int kend = min(a.K, kbeg + a.k_per_split);
 
   const uint16_t* A = (const uint16_t*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  // category bucket: the chunk's samples, their rows addressed from the start of A
+  int bfirst = 0;
+  const int brows = a.rows;  // rows per sample
+  if (a.chunks) {
+    const int4 ch = a.chunks[g];
+    if (ch.z <= 0) return;   // an unused chunk (the whole workgroup leaves before any load)
+    cat = ch.x;
+    bfirst = ch.y;
+    a.rows = ch.z * brows;
+    A = (const uint16_t*)a.A;
+  }
+  // element offset of row r of this group (bucket: row r % brows of sample perm[first + r / brows])
+  auto a_row = [&](int r) -> long {
+    if (!a.chunks) return (long)r * a.lda;
+    const int smp = a.perm[bfirst + r / brows];
+    return ((long)smp * a.a_gstride + a.a_row_off + r % brows) * a.lda;
+  };
   const uint16_t* W = (const uint16_t*)a.W + (long)cat * a.w_cstride;
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, (uint32_t)((long)a.rows * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t ra_rsrc =
+      make_rsrc(A, (uint32_t)(a.chunks ? a.map_bytes : (long)a.rows * a.lda * 2));
   const __amdgpu_buffer_rsrc_t rw_rsrc = make_rsrc(W, (uint32_t)((long)a.N * a.K * (W8 ? 1 : 2)));
 
   const int t = threadIdx.x;
@@ -508,7 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
 #pragma unroll
   for (int i = 0; i < A_I; ++i) {
     const int row = (wave * A_I + i) * RPI + lrow;
-    aoff[i] = (r0 + row < a.rows) ? (r0 + row) * (int)a.lda * 2 : OOB;
+    aoff[i] = (r0 + row < a.rows) ? (int)(a_row(r0 + row) * 2) : OOB;
     if constexpr (BK == 32) akc[i] = lkc * 8;
     else akc[i] = (lkc ^ kswz64(row & 15)) * 8;
   }
@@ -630,7 +650,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs a, Epi 
   });
   // no load may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane, PRE ? res : nullptr);
+  mfma_epilogue<BM, BN, WM, WN, EK>(a, e, acc, g, cat, split, r0, n0, wm, wn, lane, PRE ? res : nullptr, bfirst,
+                                    brows);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1216,6 +1237,15 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     // half as many workgroups fit the chip in one round
     const size_t lds = skinny_lds_bytes(a, a.rows <= 16 ? 1 : 2, 2, 8);
     return a.rows <= 16 ? skinny_lds_kind<1, 2, 8, true>(a, e, 1, lds, s) : skinny_lds_kind<2, 2, 8, true>(a, e, 1, lds, s);
+  }
+  if (a.chunks) {
+    // category buckets: 128-row tiles, one chunk of at most chunk_cap samples of `rows` rows
+    // each per tile row; stores and the Euler update only, one split
+    if (fp8 || a.ln || splits != 1 || a.rows_dev || (e.kind != EPI_STORE && e.kind != EPI_EULER) ||
+        a.chunk_cap < 1 || (long)a.chunk_cap * a.rows > 128 || a.perm == nullptr || a.map_bytes <= 0 ||
+        a.map_bytes >= (1l << 31))
+      return hipErrorInvalidValue;
+    return dma_kind<128, 64, 4, 2, 64, 4, 16>(a, e, 1, s);
   }
   if (a.rows <= 64) {
     if (a.rows <= 16) return skinny_go<1>(a, e, fp8, splits, s);

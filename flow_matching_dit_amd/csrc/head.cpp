@@ -122,7 +122,14 @@ struct Ws {  // workspace pointers
   float *sin_t, *t1, *temb, *stemb, *ada, *tauemb, *c2tab;
   uint8_t* q8;  // W8A8: e4m3 input rows of the current GEMM
   float* qs;    // W8A8: their row scales
+  int* perm;    // category buckets: the samples sorted by category
+  int4* chunks; //   and the runs of at most kBucketCap samples of one category
 };
+
+// Batches of at least kBucketMinBatch samples run the per-embodiment bf16 GEMMs over category
+// buckets of at most kBucketCap samples (one 128-row tile of 16-row samples): each category's
+// weights are read once per bucket instead of once per sample.
+constexpr int kBucketCap = 8, kBucketMinBatch = 128;
 
 }  // namespace
 
@@ -227,7 +234,8 @@ int check_config(const gr00t_config* c, std::string& why) {
   if (!(c->act_dtype == GR00T_F32 || c->act_dtype == GR00T_BF16)) return bad("act_dtype must be F32 or BF16");
   if ((c->weight_dtype == GR00T_F32) != (c->act_dtype == GR00T_F32))
     return bad("F32 weights go with F32 activations, BF16/FP8 weights with BF16 activations");
-  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8 | GR00T_FLAG_PERSIST))
+  if (c->flags & ~(GR00T_FLAG_STRICT | GR00T_FLAG_USE_GRAPH | GR00T_FLAG_W8A8 | GR00T_FLAG_PERSIST |
+                   GR00T_FLAG_NO_BUCKETS))
     return bad("unknown flag bits");
   if ((c->flags & GR00T_FLAG_W8A8) && c->weight_dtype != GR00T_FP8_E4M3)
     return bad("GR00T_FLAG_W8A8 needs FP8_E4M3 weights");
@@ -577,10 +585,28 @@ hipError_t gemm_q8(gr00t_head* h, const GemmArgs& a_in, const Epi& e, hipStream_
   return launch_gemm_a8(a, e, s);
 }
 
+bool use_buckets(const gr00t_head* h, int B) {
+  return !(h->cfg.flags & GR00T_FLAG_NO_BUCKETS) && B >= kBucketMinBatch && h->act == DT_BF16 &&
+         h->cfg.weight_dtype != GR00T_F32;
+}
+
 hipError_t gemm(gr00t_head* h, const GemmArgs& a, const Epi& e, DType at, DType wt, hipStream_t s) {
   if (use_a8(h, at, wt)) return gemm_a8(h, a, e, s);
-  if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 && a.N % 4 == 0)
+  if (at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 && a.N % 4 == 0) {
+    // one group per sample with the sample's category (per-embodiment linear): over buckets
+    if (wt == DT_BF16 && a.groups > 1 && a.ids == h->w.ids && use_buckets(h, a.groups) &&
+        (e.kind == EPI_STORE || e.kind == EPI_EULER) && a.rows * kBucketCap <= 128) {
+      GemmArgs b = a;
+      b.chunks = h->w.chunks;
+      b.perm = h->w.perm;
+      b.chunk_cap = kBucketCap;
+      b.groups = bucket_max_chunks(a.groups, h->cfg.num_categories, kBucketCap);
+      b.ids = nullptr;
+      b.map_bytes = ((long)(a.groups - 1) * a.a_gstride + a.a_row_off + a.rows) * a.lda * 2;
+      return launch_gemm_mfma(b, e, wt, s);
+    }
     return launch_gemm_mfma(a, e, wt, s);
+  }
   return launch_gemm_valu(a, e, at, wt, s);
 }
 
@@ -798,6 +824,8 @@ int run_prologue(gr00t_head* h, const gr00t_inputs* in, hipStream_t s, bool reus
   const DType kvw = (c.weight_dtype == GR00T_FP8_E4M3) ? DT_FP8 : mw;
   LAUNCH(h, s, K_SMALL, launch_sanitize_ids(in->embodiment_id, h->w.ids, h->w.bad, B, c.num_categories, s,
                                             h->w.bad_count));
+  if (use_buckets(h, B))
+    LAUNCH(h, s, K_SMALL, launch_bucket_ids(h->w.ids, B, c.num_categories, kBucketCap, h->w.perm, h->w.chunks, s));
   if (!reuse_vl) {
     h->kv_B = h->kv_L = 0;  // no valid cache until the projection below is enqueued
     LAUNCH(h, s, K_SMALL, launch_mask_codes(in->vl_mask, in->image_mask, h->w.code, B * L, s));
@@ -1320,7 +1348,9 @@ int gr00t_finalize(gr00t_head* h) {
       {(void**)&h->w.ada, K * (Nl + 1) * 2 * D * 4},                              {(void**)&h->w.tauemb, K * D * 4},
       {(void**)&h->w.c2tab, K * C * D * 4},
       {(void**)&h->w.q8, w8a8 ? std::max(Bm * Lm * E, Bm * S * std::max(F, D)) : 0},
-      {(void**)&h->w.qs, w8a8 ? std::max(Bm * Lm, Bm * S) * 4 : 0}};
+      {(void**)&h->w.qs, w8a8 ? std::max(Bm * Lm, Bm * S) * 4 : 0},
+      {(void**)&h->w.perm, Bm * 4},
+      {(void**)&h->w.chunks, (size_t)bucket_max_chunks((int)Bm, (int)C, kBucketCap) * sizeof(int4)}};
   size_t total = 0;
   for (auto& r : req) total += (r.second + 255) & ~(size_t)255;
   if (hipMalloc((void**)&h->wsbase, total) != hipSuccess) {

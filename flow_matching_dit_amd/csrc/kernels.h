@@ -44,6 +44,16 @@ struct GemmArgs {
   int ln;
   const float* ln_ada;
   const float* ascale;  // W8A8 (launch_gemm_a8): per-row fp32 scales of the e4m3 A rows, NULL otherwise
+  // Category buckets (bf16 MFMA GEMMs over many samples): group g of the launch is chunk g of
+  // a counting sort of the samples by category (launch_bucket_ids): chunks[g] = (category,
+  // first index into perm, samples, 0), no samples = nothing to do. Its rows are the `rows`
+  // rows of each of those samples (sample s: A rows s * a_gstride + a_row_off + 0 .., output
+  // group s), so the category's weights are read once per chunk instead of once per sample.
+  // map_bytes: bytes of A the samples' rows span. NULL: group g is one sample.
+  const int4* chunks;
+  const int* perm;
+  int chunk_cap;        // samples per chunk at most (chunk_cap * rows <= the tile's rows)
+  long map_bytes;
 };
 
 struct Epi {
@@ -138,6 +148,12 @@ hipError_t launch_mask_codes(const uint8_t* vl_mask, const uint8_t* image_mask, 
                              hipStream_t s);
 // ids_out[b] = ids_in[b] if in [0, C) else 0; bad[b] = out of range; *bad_count (when given) is
 // increased by the number of out-of-range ids (a monotonic count across calls).
+// Counting sort of the B sanitised ids (in [0, C)) by category, stable: perm lists the samples
+// of category 0 in sample order, then category 1, ...; chunks[j] (j < maxch = ceil(B / cap) +
+// min(B, C)) splits each category's run into runs of at most cap samples, (category, first
+// index into perm, samples, 0), the unused entries (0, 0, 0, 0). One workgroup.
+hipError_t launch_bucket_ids(const int* ids, int B, int C, int cap, int* perm, int4* chunks, hipStream_t s);
+inline int bucket_max_chunks(int B, int C, int cap) { return (B + cap - 1) / cap + (B < C ? B : C); }
 hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, int B, int C,
                                hipStream_t s, unsigned* bad_count = nullptr);
 // dst rows (b * dst_stride_rows + dst_row_off) <- src rows b (fp32, width D).

@@ -744,6 +744,61 @@ hipError_t launch_sanitize_ids(const int* ids_in, int* ids_out, uint8_t* bad, in
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(1024) void bucket_ids_kernel(const int* ids, int B, int C, int cap, int* perm,
+                                                         int4* chunks, int maxch) {
+  extern __shared__ int bsh[];  // count[C], first sample[C + 1], first chunk[C + 1]
+  int* cnt = bsh;
+  int* first = bsh + C;
+  int* cfirst = first + C + 1;
+  const int t = threadIdx.x;
+  for (int c = t; c < C; c += blockDim.x) cnt[c] = 0;
+  __syncthreads();
+  for (int b = t; b < B; b += blockDim.x) atomicAdd(&cnt[ids[b]], 1);
+  __syncthreads();
+  if (t == 0) {
+    int f = 0, fc = 0;
+    for (int c = 0; c < C; ++c) {
+      first[c] = f;
+      cfirst[c] = fc;
+      f += cnt[c];
+      fc += (cnt[c] + cap - 1) / cap;
+    }
+    first[C] = f;
+    cfirst[C] = fc;
+  }
+  __syncthreads();
+  // rank of sample b among the samples of its category (stable order)
+  for (int b = t; b < B; b += blockDim.x) {
+    const int id = ids[b];
+    int rank = 0;
+    for (int q = 0; q < b; ++q) rank += ids[q] == id ? 1 : 0;
+    perm[first[id] + rank] = b;
+  }
+  for (int j = t; j < maxch; j += blockDim.x) {
+    int4 ch = make_int4(0, 0, 0, 0);
+    if (j < cfirst[C]) {
+      int lo = 0, hi = C - 1;  // the category whose chunks hold j: last c with cfirst[c] <= j
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (cfirst[mid] <= j) lo = mid;
+        else hi = mid - 1;
+      }
+      const int k = j - cfirst[lo];
+      ch = make_int4(lo, first[lo] + k * cap, min(cap, cnt[lo] - k * cap), 0);
+    }
+    chunks[j] = ch;
+  }
+}
+
+hipError_t launch_bucket_ids(const int* ids, int B, int C, int cap, int* perm, int4* chunks, hipStream_t s) {
+  if (B <= 0 || C <= 0 || cap <= 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(3 * C + 2) * sizeof(int);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bucket_ids_kernel, dim3(1), dim3(1024), lds, s, ids, B, C, cap, perm, chunks,
+                     bucket_max_chunks(B, C, cap));
+  return hipGetLastError();
+}
+
 __global__ void copy_rows_kernel(const float* src, long src_ld, float* dst, long dst_ld, long dst_gstride,
                                  int dst_row_off, int D) {
   const int b = blockIdx.y;

@@ -20,6 +20,7 @@ FLAG_STRICT = 0x1
 FLAG_USE_GRAPH = 0x2
 FLAG_W8A8 = 0x4
 FLAG_PERSIST = 0x8
+FLAG_NO_BUCKETS = 0x10
 
 STATUS = {
     0: "OK", -1: "E_INVALID_ARG", -2: "E_SHAPE", -3: "E_EMBODIMENT", -4: "E_NOT_FINALIZED",

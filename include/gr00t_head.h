@@ -81,6 +81,16 @@ typedef enum gr00t_dtype {
                                    the next call reports GR00T_E_DEVICE and the handle falls back
                                    to the launch-per-step path. Ignored where it does not apply. */
 
+#define GR00T_FLAG_NO_BUCKETS 0x10u /* batches of 128 samples or more normally run the
+                                       per-embodiment bf16 linears over category buckets (the
+                                       samples sorted by embodiment id on the device, each
+                                       category's weights read once per bucket of up to 8
+                                       samples; "Model architecture", Embodiment-specific
+                                       projectors, CategorySpecificLinear: W[cat_ids] then a
+                                       batched product). With this flag every sample gathers its
+                                       own category's weights, as for smaller batches; for
+                                       comparison */
+
 /*
  * Model and capacity. Widths follow the "Model configuration" table of the
  * architecture page: hidden = num_heads * head_dim is used for the state and

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -23,6 +24,7 @@
 #include <new>
 #include <string>
 #include <thread>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -133,6 +135,15 @@ constexpr int kBucketCap = 8, kBucketMinBatch = 128;
 
 }  // namespace
 
+// Shape and buffers of a get_action call: a captured whole call replays with exactly these.
+struct CallKey {
+  int B = 0, L = 0;
+  std::array<const void*, 9> p{};
+  bool operator<(const CallKey& o) const { return std::tie(B, L, p) < std::tie(o.B, o.L, o.p); }
+  bool operator==(const CallKey& o) const { return B == o.B && L == o.L && p == o.p; }
+};
+constexpr size_t kMaxCallGraphs = 8;
+
 struct gr00t_head {
   gr00t_config cfg{};
   int device = 0;
@@ -148,6 +159,11 @@ struct gr00t_head {
   Ws w{};
   hipStream_t cap_stream = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  // whole-call graphs (prologue, K steps, output) keyed by the call's shape and buffers; the
+  // buffers of the previous call (a call whose buffers repeat is captured)
+  std::map<CallKey, hipGraphExec_t> call_graphs;
+  std::vector<CallKey> call_order;  // capture order, for eviction
+  CallKey last_call{};
   uint64_t calls = 0;
   // Deferred report of invalid ids (non-strict mode). Every call copies the device count of
   // invalid ids met so far and its per-sample flags into the next of kReportSlots pinned slots
@@ -487,12 +503,12 @@ void pack(gr00t_head* h, Spec& s, const void* data, gr00t_dtype dt) {
 
 enum KClass {
   K_VLLN = 0, K_KV_PROJ, K_STATE_ENC, K_ACTION_ENC, K_ADALN, K_QKV_PROJ, K_Q_PROJ, K_ATTN_SELF, K_ATTN_CROSS,
-  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_GRAPH, K_BLOCKS, K_NCLASS
+  K_O_PROJ, K_NORM3, K_FF_UP, K_FF_DOWN, K_OUT_PROJ, K_DECODER, K_SMALL, K_GRAPH, K_BLOCKS, K_CALL_GRAPH, K_NCLASS
 };
 const char* const kClassNames[K_NCLASS] = {"vlln", "kv_proj", "state_enc", "action_enc", "adaln", "qkv_proj",
                                            "q_proj", "attn_self", "attn_cross", "o_proj", "norm3", "ff_up",
                                            "ff_down", "out_proj", "decoder", "small", "steps_graph",
-                                           "blocks_b1"};
+                                           "blocks_b1", "call_graph"};
 
 // Returns the index of the start event recorded on s, or -1 when not profiling.
 int prof_begin(gr00t_head* h, hipStream_t s) {
@@ -1419,6 +1435,44 @@ int gr00t_prepare(gr00t_head* h, int32_t batch, int32_t vl_len) {
   return GR00T_OK;
 }
 
+// Capture prologue, K steps and output of a call with these buffers as one graph (evicting the
+// oldest of kMaxCallGraphs; the device is synchronised first, as the evicted graph may still run).
+static int capture_call(gr00t_head* h, const gr00t_inputs* in, float* action_pred, const CallKey& k) {
+  if (h->call_graphs.size() >= kMaxCallGraphs) {
+    HIPCHK(h, hipDeviceSynchronize());
+    (void)hipGraphExecDestroy(h->call_graphs[h->call_order.front()]);
+    h->call_graphs.erase(h->call_order.front());
+    h->call_order.erase(h->call_order.begin());
+  }
+  const int kv_B = h->kv_B, kv_L = h->kv_L;
+  hipGraph_t g = nullptr;
+  HIPCHK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  const bool prof = h->prof_on;
+  h->prof_on = false;  // no event records inside the graph
+  int rc = run_prologue(h, in, h->cap_stream, false);
+  if (rc == GR00T_OK) rc = run_steps(h, in->batch, in->vl_len, 0, h->cfg.num_steps, true, h->cap_stream);
+  hipError_t e = hipSuccess;
+  if (rc == GR00T_OK)
+    e = launch_output(h->w.x, in->action_mask, h->w.bad, action_pred, in->batch,
+                      h->cfg.action_horizon * h->cfg.action_dim, h->cap_stream);
+  h->prof_on = prof;
+  h->kv_B = kv_B;  // nothing ran yet: the caches are those of before
+  h->kv_L = kv_L;
+  hipError_t ee = hipStreamEndCapture(h->cap_stream, &g);
+  if (rc != GR00T_OK || e != hipSuccess || ee != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    if (rc != GR00T_OK) return rc;
+    return fail(h, GR00T_E_HIP, std::string("whole-call capture failed: ") + hipGetErrorString(e != hipSuccess ? e : ee));
+  }
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(h, GR00T_E_HIP, std::string("hipGraphInstantiate failed: ") + hipGetErrorString(e));
+  h->call_graphs[k] = ex;
+  h->call_order.push_back(k);
+  return GR00T_OK;
+}
+
 static int get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred, void* hip_stream, bool reuse_vl) {
   int rc = check_inputs(h, in, action_pred, reuse_vl);
   if (rc != GR00T_OK) return rc;
@@ -1432,6 +1486,31 @@ static int get_action(gr00t_head* h, const gr00t_inputs* in, float* action_pred,
   HIPCHK(h, hipSetDevice(h->device));
   rc = pre_call_checks(h, in, s);
   if (rc != GR00T_OK) return rc;
+  // A full call with caller noise on a prepared shape whose buffers repeat those of the previous
+  // call replays one graph of the whole call (captured on that repetition).
+  if (have_graph && !reuse_vl && in->noise) {
+    CallKey k;
+    k.B = in->batch;
+    k.L = in->vl_len;
+    k.p = {in->vl_features, in->vl_mask, in->image_mask, in->state, in->embodiment_id, in->noise, in->action_mask,
+           in->state_features_out, action_pred};
+    auto it = h->call_graphs.find(k);
+    if (it == h->call_graphs.end() && k == h->last_call) {
+      rc = capture_call(h, in, action_pred, k);
+      if (rc != GR00T_OK) return rc;
+      it = h->call_graphs.find(k);
+    }
+    h->last_call = k;
+    if (it != h->call_graphs.end()) {
+      LAUNCH(h, s, K_CALL_GRAPH, hipGraphLaunch(it->second, s));
+      h->kv_B = in->batch;  // the replayed prologue rebuilt the VL key/value caches
+      h->kv_L = in->vl_len;
+      rc = enqueue_report(h, in->batch, s);
+      if (rc != GR00T_OK) return rc;
+      h->calls++;
+      return GR00T_OK;
+    }
+  }
   rc = run_prologue(h, in, s, reuse_vl);
   if (rc != GR00T_OK) return rc;
   if (have_graph) {
@@ -1509,6 +1588,7 @@ void gr00t_destroy(gr00t_head* h) {
     (void)hipDeviceSynchronize();  // copies into the pinned report slots may still be in flight
   }
   for (auto& kv : h->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : h->call_graphs) (void)hipGraphExecDestroy(kv.second);
   if (h->cap_stream) {
     (void)hipStreamSynchronize(h->cap_stream);
     (void)hipStreamDestroy(h->cap_stream);

@@ -62,7 +62,16 @@ typedef enum gr00t_dtype {
                                      graph mode, an unprepared shape is refused (E_UNCAPTURED).
                                      Shapes and dtypes of the tensors behind the pointers are
                                      checked by the Python binding, which knows them. */
-#define GR00T_FLAG_USE_GRAPH 0x2u /* replay the K-step loop from a captured hipGraph */
+#define GR00T_FLAG_USE_GRAPH 0x2u /* replay the K-step loop from a captured hipGraph (see
+                                     gr00t_prepare); a gr00t_get_action on a prepared shape
+                                     with inputs.noise given, whose buffers (every pointer of
+                                     gr00t_inputs and action_pred) are those of the previous
+                                     call, is captured as one graph of the whole call (prologue,
+                                     K steps, output) and replayed whenever those buffers come
+                                     again; up to 8 such graphs per handle, the oldest evicted
+                                     (the device is synchronised first). Buffer contents are read
+                                     at each replay; a buffer freed and reallocated at the same
+                                     address is simply reused. */
 #define GR00T_FLAG_W8A8 0x4u      /* with FP8_E4M3 weights: the input rows of every e4m3-weight
                                      GEMM (the DiT's q, k, v, o, MLP and output projections and
                                      the VL key/value projection) are quantised to e4m3 with one

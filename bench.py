@@ -257,6 +257,29 @@ def headline_leg(args, w, weights, inputs, noise, H, synth):
     return total_s, wall, dev, prof, first.cpu().numpy(), reuse_s, train_s, b1_res
 
 
+def persist_leg(args, weights, H, synth):
+    """B = 1 latency with the opt-in persistent block kernel (GR00T_FLAG_PERSIST: every DiT block
+    of an Euler step in one launch): wall / device times of synchronised calls and the per-launch
+    pass."""
+    import torch
+    b1 = synth.WORKLOADS[args.b1_workload]
+    inputs, noise = synth.make_inputs(b1), synth.make_noise(b1)
+    h = H.Gr00tHead(b1.cfg, max_batch=1, max_vl_len=b1.vl_len, flags=H.FLAG_USE_GRAPH | H.FLAG_PERSIST)
+    h.load_weights(weights).finalize()
+    h.prepare(1, b1.vl_len)
+    d = H.device_inputs(inputs, noise, h.act_torch_dtype)
+    o = torch.empty((1, b1.cfg.action_horizon, b1.cfg.action_dim), dtype=torch.float32, device="cuda:0")
+    call = lambda: h.get_action(**d, out=o)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    wall, dev = timed_calls(call, args.b1_steps)
+    prof = per_launch_pass(h, call, 1)
+    h.close()
+    log(f"[bench] {b1.name} with GR00T_FLAG_PERSIST: p50 {statistics.median(wall):.3f} ms")
+    return wall, dev, prof
+
+
 def sub_categories(weights, C):
     """The first C categories of every per-embodiment table (leading category axis)."""
     out = {}
@@ -430,6 +453,8 @@ def main():
     ap.add_argument("--config-calls", type=int, default=10,
                     help="synchronised calls per other configuration (0: skip those legs)")
     ap.add_argument("--profile-calls", type=int, default=2)
+    ap.add_argument("--no-b1-persist", dest="b1_persist", action="store_false",
+                    help="skip the B = 1 leg with the opt-in persistent block kernel")
     ap.add_argument("--cpu-samples", type=int, default=0, help="oracle samples (0: the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variants", action="store_true",
@@ -482,6 +507,18 @@ def main():
                                "what": "weights of every layer read once per Euler step, the K/V projection "
                                        "weights and the VL features once per call, activations once"},
                           breakdown={c: {"launches": v[0], "ms": round(v[1], 4)} for c, v in prof_b1.items() if v[0]})
+        if args.b1_persist:
+            pw, pd, pprof = persist_leg(args, weights, H, synth)
+            pp50 = statistics.median(pw)
+            n, ms = pprof.get("blocks_b1", (0, 0.0))
+            latency_b1["persistent"] = dict(
+                flags="GR00T_FLAG_PERSIST", **stats(pw), device=stats(pd),
+                hbm={"algorithmic_bytes": byts, "achieved_gbs": round(byts / (pp50 * 1e-3) / 1e9, 1),
+                     "frac": round(byts / (pp50 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                blocks_kernel={"launches_per_call": n, "avg_launch_ms": round(ms / n, 4) if n else None,
+                               "what": "one launch per Euler step running every DiT block (eager per-launch "
+                                       "pass)"},
+                breakdown={c: {"launches": v[0], "ms": round(v[1], 4)} for c, v in pprof.items() if v[0]})
     if args.config_calls:
         c3_w = {}
 

@@ -1546,6 +1546,22 @@ int gr00t_train_forward_noalloc(gr00t_head* h, const gr00t_inputs* in, const flo
   return train_forward(h, in, actions, t, loss, v_pred, hip_stream, true);
 }
 
+#ifdef GR00T_PHASE_TRACE
+// Diagnostic builds only (flow_matching_dit_amd/phase_trace.py): copy the persistent kernel's
+// phase timestamps of its last launch (persist_trace_words() values, s_memrealtime at 100 MHz)
+// to the host. Synchronous.
+int gr00t_persist_phase_trace(gr00t_head* h, uint64_t* host, int32_t n) {
+  if (!h || !host || n < persist_trace_words()) return GR00T_E_INVALID_ARG;
+  if (!h->persist_base) return fail(h, GR00T_E_INVALID_ARG, "the handle has no persistent kernel");
+  PersistArgs pa{};
+  persist_bind_scratch(pa, h->persist_base);
+  HIPCHK(h, hipSetDevice(h->device));
+  HIPCHK(h, hipDeviceSynchronize());
+  HIPCHK(h, hipMemcpy(host, pa.trace, sizeof(uint64_t) * persist_trace_words(), hipMemcpyDeviceToHost));
+  return GR00T_OK;
+}
+#endif
+
 int gr00t_velocity(gr00t_head* h, const gr00t_inputs* in, int32_t step_k, float* v, void* hip_stream) {
   int rc = check_inputs(h, in, v);
   if (rc != GR00T_OK) return rc;

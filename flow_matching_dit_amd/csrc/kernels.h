@@ -221,7 +221,10 @@ struct PersistArgs {
   float* part;
   float2* statx;
   unsigned* ctl;
+  unsigned long long* trace;  // phase timestamps (written by GR00T_PHASE_TRACE builds only)
 };
+// Words of the phase timestamp area (2 workgroups x 64 blocks x 16 boundaries).
+constexpr int persist_trace_words() { return 2 * 64 * 16; }
 // Whether the persistent kernel serves this shape (model widths, rows, VL length, CU count).
 bool persist_b1_fits(int D, int F, int nh, int hd, int S, int L, int num_cus);
 size_t persist_scratch_bytes();

@@ -85,6 +85,22 @@ __device__ __forceinline__ void vm_wait() {
 }
 // drop this CU's L1 lines: data other CUs of the XCD wrote is then read from the XCD's L2
 __device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+// Phase timestamps (builds with GR00T_PHASE_TRACE only): s_memrealtime (100 MHz) at the phase
+// boundaries k = 0 .. 15 of every block, in workgroups (XCD 0, ticket 0) and (XCD 7, ticket 31),
+// to trace[(which * PTRACE_BLOCKS + block) * 16 + k]; each launch overwrites the last one's.
+constexpr int PTRACE_BLOCKS = 64;
+#ifdef GR00T_PHASE_TRACE
+#define PTS(k)                                                                                          \
+  do {                                                                                                  \
+    if (threadIdx.x == 0 && l < PTRACE_BLOCKS && ((x == 0 && li == 0) || (x == NX - 1 && li == NWG - 1))) \
+      a.trace[((x == NX - 1) * PTRACE_BLOCKS + l) * 16 + (k)] = __builtin_amdgcn_s_memrealtime();      \
+  } while (0)
+#else
+#define PTS(k) \
+  do {         \
+  } while (0)
+#endif
+
 __device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 0xFu; }
 
 // device-coherent 16-byte load / store (sc1): the partial sums other XCDs exchange
@@ -589,8 +605,10 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
     const int t = opaque(threadIdx.x), lane = t & 63, lr = lane & 15, lg = lane >> 4;
     const bool hown = (t & 15) < 12 && t / 16 < S;
     const int hrow = t / 16, hcol = CW * li + 4 * (t & 15);
+    PTS(0);
     // ---- adaLN of h into the staged rows (block 0: the residual stream as the step starts)
     ln_rows(hx, statx, a.ada + (size_t)l * 2 * PD, S, nl, rstat, t);
+    PTS(1);
     // ---- q (cross) or q, k, v (self) of this XCD's heads, the workgroup's 6 (18) columns
     zero_acc(acc);
     if (cw) mma_lds<2>(wa, nl, S, wave, lane, acc);
@@ -610,12 +628,16 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
         }
       }
     }
+    PTS(2);
     ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w1<0, 3>(wa, B.w1, x, li, wave, lane); });
     if (!ok) break;
+    PTS(3);
     // ---- attention of one head for up to 4 queries
     attention_head(a, self, cross_idx, (l % (2 * a.text_every) == 0) ? 1 : 2, x, li, t, asc);
+    PTS(4);
     ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w1<3, KQ>(wa, B.w1, x, li, wave, lane); });
     if (!ok) break;
+    PTS(5);
     // ---- o projection: this XCD's partial sum over its 192 attention columns, for the
     //      workgroup's 48 output columns; then the MLP up and down weights are requested
     zero_acc(acc);
@@ -639,8 +661,10 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
           st_sc1(rpart, (((par * NX + x) * SMAX + tok) * PD + n) * 4, make_float4(sum[0], sum[1], sum[2], sum[3]));
       }
     }
+    PTS(6);
     ok = pbarrier<true>(ctl, x, nbd, &sflag, [&] { load_w2<0, 2>(wb, B.w2, x, li, wave, lane); });
     if (!ok) break;
+    PTS(7);
     // ---- residual: h += sum over the XCDs' partials (fixed order) + bo
     if (hown) {
       float4 p = ld_sc1(rpart, (((par * NX + 0) * SMAX + hrow) * PD + hcol) * 4);
@@ -660,10 +684,13 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
     }
     publish_h(hs, hown, hrow, hcol, t, S, hx, stat_wg);
     par ^= 1;
+    PTS(8);
     ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w2<2, KD>(wb, B.w2, x, li, wave, lane); });
     if (!ok) break;
+    PTS(9);
     // ---- LayerNorm, MLP up + GELU for the workgroup's 24 MLP columns
     ln_rows(hx, statx, nullptr, S, nl, rstat, t);
+    PTS(10);
     zero_acc(acc);
     if (cw) mma_lds<2>(wa, nl, S, wave, lane, acc);
     {
@@ -679,10 +706,12 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
         }
       }
     }
+    PTS(11);
     ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] {
       if (more) load_wq<0, 3>(wa, uniform(a.blocks[l + 1].wq), a.blocks[l + 1].nq == 3, x, li, wave, lane);
     });
     if (!ok) break;
+    PTS(12);
     // ---- MLP down: this XCD's partial sum over its 768 MLP columns, for the workgroup's 48
     //      output columns; then the next block's q / q,k,v and o projection weights are requested
     zero_acc(acc);
@@ -711,6 +740,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
           st_sc1(rpart, (((par * NX + x) * SMAX + tok) * PD + n) * 4, make_float4(sum[0], sum[1], sum[2], sum[3]));
       }
     }
+    PTS(13);
     ok = pbarrier<true>(ctl, x, nbd, &sflag, [&] {
       if (more) {
         const PBlock Bn = uniform_block(a.blocks, l + 1);
@@ -719,6 +749,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
       }
     });
     if (!ok) break;
+    PTS(14);
     if (hown) {
       float4 p = ld_sc1(rpart, (((par * NX + 0) * SMAX + hrow) * PD + hcol) * 4);
 #pragma unroll
@@ -739,6 +770,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
     par ^= 1;
     if (!self) ++cross_idx;
     if (more) ok = pbarrier<false>(ctl, x, nbx, &sflag);
+    PTS(15);
   }
   // the residual stream after the last block (every workgroup holds its 48 columns)
   if (ok && (t & 15) < 12 && t / 16 < S) *(float4*)(a.h + (t / 16) * PD + CW * li + 4 * (t & 15)) = hs;
@@ -773,7 +805,8 @@ size_t persist_scratch_bytes() {
          (size_t)NX * SMAX * FX * 2 +                        // ux
          (size_t)2 * NX * SMAX * PD * 4 +                    // part
          (size_t)NX * NWG * SMAX * 8 +                       // statx
-         (size_t)C_WORDS * 4;                                // ctl
+         (size_t)C_WORDS * 4 +                               // ctl
+         (size_t)2 * PTRACE_BLOCKS * 16 * 8;                 // phase timestamps
 }
 
 void persist_bind_scratch(PersistArgs& a, void* base) {
@@ -791,6 +824,8 @@ void persist_bind_scratch(PersistArgs& a, void* base) {
   a.statx = (float2*)p;
   p += (size_t)NX * NWG * SMAX * 8;
   a.ctl = (unsigned*)p;
+  p += (size_t)C_WORDS * 4;
+  a.trace = (unsigned long long*)p;
 }
 
 unsigned* persist_error_word(const PersistArgs& a) { return a.ctl + C_ERR; }

@@ -204,6 +204,73 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmArgs a, Epi e) {
   }
 }
 
+// Vector-ALU GEMM for at most 32 rows: the 64 x 64 tile leaves a handful of workgroups each
+// walking all of K. Here a workgroup owns 4 output columns and its 256 threads split K into
+// 64 slices (thread t: column t % 4, k = 4 (t / 4) + 256 i .. +3, loaded as one vector, every
+// row in registers); the slices' partial sums are added in slice order through LDS. Needs
+// K and lda multiples of 4 (vector loads).
+constexpr int VS_COLS = 4, VS_SLICES = 64, VS_ROWS = 32;
+template <typename T>
+__device__ __forceinline__ void ld4(const T* p, float (&v)[4]);
+template <>
+__device__ __forceinline__ void ld4<float>(const float* p, float (&v)[4]) {
+  const float4 f = *(const float4*)p;
+  v[0] = f.x;
+  v[1] = f.y;
+  v[2] = f.z;
+  v[3] = f.w;
+}
+template <>
+__device__ __forceinline__ void ld4<bf16>(const bf16* p, float (&v)[4]) {
+  const uint2 u = *(const uint2*)p;
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+template <typename TA, typename TW, int EK>
+__global__ __launch_bounds__(256) void gemm_valu_skinny_kernel(GemmArgs a, Epi e) {
+  __shared__ float red[VS_SLICES][VS_ROWS][VS_COLS + 1];
+  if (a.rows_dev) a.rows = min(a.rows, *a.rows_dev);
+  const int g = blockIdx.z;
+  const int cat = a.ids ? a.ids[g] : 0;
+  const int t = threadIdx.x, c = t % VS_COLS, sl = t / VS_COLS;
+  const int n = blockIdx.x * VS_COLS + c;
+  const TA* A = (const TA*)a.A + ((long)g * a.a_gstride + a.a_row_off) * a.lda;
+  const TW* W = (const TW*)a.W + (long)cat * a.w_cstride;
+  float acc[VS_ROWS];
+#pragma unroll
+  for (int r = 0; r < VS_ROWS; ++r) acc[r] = 0.0f;
+  if (n < a.N) {
+    const TW* wr = W + (long)n * a.K;
+    for (int k0 = 4 * sl; k0 < a.K; k0 += 4 * VS_SLICES) {
+      float wv[4];
+      ld4(wr + k0, wv);
+#pragma unroll
+      for (int r = 0; r < VS_ROWS; ++r) {
+        if (r >= a.rows) break;
+        float av[4];
+        ld4(A + (long)r * a.lda + k0, av);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[r] = fmaf(av[q], wv[q], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < VS_ROWS; ++r) red[sl][r][c] = acc[r];
+  __syncthreads();
+  for (int p = t; p < a.rows * VS_COLS; p += 256) {
+    const int r = p / VS_COLS, cc = p % VS_COLS, nn = blockIdx.x * VS_COLS + cc;
+    if (nn >= a.N) continue;
+    float s = 0.0f;
+    for (int q = 0; q < VS_SLICES; ++q) s += red[q][r][cc];
+    float v[1] = {s};
+    if (a.wscale) v[0] *= a.wscale[(long)cat * a.s_cstride + nn];
+    if (a.bias) v[0] += a.bias[(long)cat * a.b_cstride + nn];
+    epi_store<EK, 1>(e, g, r, nn, v, cat, 0);
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // MFMA GEMM
 // ------------------------------------------------------------------------------------
@@ -1122,6 +1189,20 @@ static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, int split
 // ------------------------------------------------------------------------------------
 template <typename TA, typename TW>
 static hipError_t valu_go(const GemmArgs& a, const Epi& e, hipStream_t s) {
+  // few rows, deep K: split K inside the workgroup (vector loads: K and lda multiples of 4)
+  if (a.rows <= VS_ROWS && a.K >= 4 * VS_SLICES && a.K % 4 == 0 && a.lda % 4 == 0 &&
+      ((uintptr_t)a.A % 16) == 0 && ((uintptr_t)a.W % 16) == 0 && (a.w_cstride % 4) == 0 && (a.a_gstride * a.lda) % 4 == 0 &&
+      ((long)a.a_row_off * a.lda) % 4 == 0) {
+    dim3 grid((a.N + VS_COLS - 1) / VS_COLS, 1, a.groups);
+    switch (e.kind) {
+      case EPI_STORE: hipLaunchKernelGGL((gemm_valu_skinny_kernel<TA, TW, EPI_STORE>), grid, dim3(256), 0, s, a, e); break;
+      case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_valu_skinny_kernel<TA, TW, EPI_RESID_ADD>), grid, dim3(256), 0, s, a, e); break;
+      case EPI_HEADS: hipLaunchKernelGGL((gemm_valu_skinny_kernel<TA, TW, EPI_HEADS>), grid, dim3(256), 0, s, a, e); break;
+      case EPI_EULER: hipLaunchKernelGGL((gemm_valu_skinny_kernel<TA, TW, EPI_EULER>), grid, dim3(256), 0, s, a, e); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((a.N + 63) / 64, (a.rows + 63) / 64, a.groups);
   switch (e.kind) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_valu_kernel<TA, TW, EPI_STORE>), grid, dim3(256), 0, s, a, e); break;

@@ -456,7 +456,21 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
   // a second tile past the end reloads the last one and is not used), so the mask and the
   // tiles cost one memory latency, not two.
   const int ntiles = (Lk + 31) / 32;
-  for (int kt = wave; kt < ntiles; kt += 2 * NW) {
+  if constexpr (QF >= 3) {
+    // many query fragments (long horizons): one tile at a time, so that the registers allow
+    // two waves per SIMD
+    for (int kt = wave; kt < ntiles; kt += NW) {
+      bf16x8_v kf0[2][KS], vf0[HF];
+      attn_load_tile<HD>(kr, vr, Lp, kt, g, c16, kf0, vf0);
+      asm volatile("" ::: "memory");
+      const uint8_t mb0 = buf_load1(mr, kt * 32 + (lane & 31));
+      const bool ad0 = lane < 32 && kt * 32 + lane < Lk && (a.mask == nullptr || (mb0 & a.mask_bit) != 0);
+      const unsigned long long bal0 = __ballot(ad0);
+      const uint32_t bits0 = (uint32_t)(bal0 >> (8 * g)) & 0xFFu;
+      if (bal0) attn_tile<HD, QF>(qfr, acc, m, l, kf0, vf0, bits0, (uint32_t)bal0 == 0xFFFFFFFFu, sl2);
+    }
+  }
+  for (int kt = wave; QF < 3 && kt < ntiles; kt += 2 * NW) {
     const int kt2 = kt + NW;
     bf16x8_v kf0[2][KS], vf0[HF], kf1[2][KS], vf1[HF];
     attn_load_tile<HD>(kr, vr, Lp, kt, g, c16, kf0, vf0);

@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) void attention_mfma_kernel(AttnArgs a) {
 constexpr int AW_MAXWORDS = 8;  // keys per pair <= 512 (one mask byte per lane and word)
 constexpr int AW_SETS = 2;  // register sets of the key-tile ring (deeper rings cost occupancy)
 template <int HD, int QF, int NS, bool MASK>
-__global__ __launch_bounds__(256) void attention_wave_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attention_wave_kernel(AttnArgs a) {
   constexpr int KS = (HD + 31) / 32, HF = HD / 16;
   __shared__ unsigned long long words_s[4][AW_MAXWORDS];
   const int t = threadIdx.x, lane = t & 63;

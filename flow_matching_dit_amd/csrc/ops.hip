@@ -175,9 +175,109 @@ __global__ __launch_bounds__(256) void resid_layernorm_kernel(float* __restrict_
   }
 }
 
+// The same for bf16 / fp32 outputs with one workgroup of NW waves per row: thread t owns
+// columns 2 t + 128 NW i .. +1, so NW waves share a row and NW times as many loads are in
+// flight as with a wave per row (at B = 64 the 1088 rows give about one wave per SIMD). The
+// row's sums are wave sums added in wave order through LDS.
+template <typename TY, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void resid_layernorm_row_kernel(float* __restrict__ h, const float* __restrict__ part,
+                                                                      long split_stride, TY* __restrict__ y, int D,
+                                                                      const float* __restrict__ ada_base, int ada_rows,
+                                                                      long ada_stride) {
+  constexpr int NTR = 64 * NW, MAXV = (2048 + 2 * NTR - 1) / (2 * NTR);  // float2 per thread, up to 2048 columns
+  __shared__ float red[2][NW];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const float* ada = ada_base ? ada_base + (ada_rows > 0 ? (long)(row / ada_rows) * ada_stride : 0) : nullptr;
+  float* hr = h + (long)row * D;
+  float2 v[MAXV];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = 2 * t + 2 * NTR * i;
+    float2 x = make_float2(0.0f, 0.0f);
+    if (c < D) {
+      x = *(const float2*)(hr + c);
+#pragma unroll
+      for (int p = 0; p < NS; ++p) {
+        const float2 q = *(const float2*)(part + (long)p * split_stride + (long)row * D + c);
+        x.x += q.x;
+        x.y += q.y;
+      }
+      if (NS > 0) *(float2*)(hr + c) = x;
+    }
+    v[i] = x;
+    s += x.x + x.y;
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[0][wave] = s;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red[0][w];
+  const float mean = tot / (float)D;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if (2 * t + 2 * NTR * i < D) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean;
+      s2 += a0 * a0 + a1 * a1;
+    }
+  }
+  s2 = wave_sum(s2);
+  if (lane == 0) red[1][wave] = s2;
+  __syncthreads();
+  float tot2 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot2 += red[1][w];
+  const float rstd = 1.0f / sqrtf(tot2 / (float)D + 1e-5f);
+  TY* yr = y + (long)row * D;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = 2 * t + 2 * NTR * i;
+    if (c < D) {
+      float o0 = (v[i].x - mean) * rstd, o1 = (v[i].y - mean) * rstd;
+      if (ada) {
+        const float2 sc = *(const float2*)(ada + c);
+        const float2 sh = *(const float2*)(ada + D + c);
+        o0 = o0 * (1.0f + sc.x) + sh.x;
+        o1 = o1 * (1.0f + sc.y) + sh.y;
+      }
+      if (sizeof(TY) == 4) *(float2*)((float*)yr + c) = make_float2(o0, o1);
+      else *(uint32_t*)((uint16_t*)yr + c) = bf16x2_bits(o0, o1);
+    }
+  }
+}
+
+constexpr int RLN_FEW_ROWS = 256;
 template <typename TY>
 static hipError_t resid_ln_go(float* h, const float* partials, int nsplit, long split_stride, TY* y, int rows, int D,
                               const float* ada, int ada_rows, long ada_stride, float* qscale, hipStream_t s) {
+  if (sizeof(TY) != 1) {  // bf16 / fp32 outputs: a workgroup per row (8 waves when there are few rows)
+#define GR00T_RLN_CASE(N)                                                                                       \
+  case N:                                                                                                       \
+    if (rows < RLN_FEW_ROWS)                                                                                    \
+      hipLaunchKernelGGL((resid_layernorm_row_kernel<TY, N, 8>), dim3(rows), dim3(512), 0, s, h, partials,      \
+                         split_stride, y, D, ada, ada_rows, ada_stride);                                        \
+    else                                                                                                        \
+      hipLaunchKernelGGL((resid_layernorm_row_kernel<TY, N, 4>), dim3(rows), dim3(256), 0, s, h, partials,      \
+                         split_stride, y, D, ada, ada_rows, ada_stride);                                        \
+    break;
+    switch (nsplit) {
+      GR00T_RLN_CASE(0)
+      GR00T_RLN_CASE(1)
+      GR00T_RLN_CASE(2)
+      GR00T_RLN_CASE(3)
+      GR00T_RLN_CASE(4)
+      GR00T_RLN_CASE(5)
+      GR00T_RLN_CASE(6)
+      GR00T_RLN_CASE(7)
+      GR00T_RLN_CASE(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef GR00T_RLN_CASE
+    return hipGetLastError();
+  }
   dim3 grid((rows + 3) / 4), blk(256);
   switch (nsplit) {
     case 0: hipLaunchKernelGGL((resid_layernorm_kernel<TY, 0>), grid, blk, 0, s, h, partials, split_stride, y, rows, D, ada, ada_rows, ada_stride, qscale); break;

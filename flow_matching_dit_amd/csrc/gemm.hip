@@ -972,9 +972,10 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
 // whole slice of K (at most KC k-steps) are already in flight. LN: the rows are the fp32
 // residual stream instead, normalised (GemmArgs::ln) by the waves as they stage them.
 constexpr int SKL_MAX_LDS = 64 * 1024;
-template <int MF, int NC, int NWAVE, int EK, bool LN = false>
+template <int MF, int NC, int NWAVE, int EK, int LNV = 0>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a, Epi e) {
   constexpr int KC = 8;
+  constexpr bool LN = LNV > 0;  // LN: the rows are K = 256 LNV fp32 values, normalised here
   extern __shared__ __attribute__((aligned(1024))) uint16_t skl[];
   const int g = blockIdx.y;
   const int split = blockIdx.z;
@@ -1003,18 +1004,18 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
   }
   // 1. activation rows [0, rows) x [kbeg, kbeg + kper) -> LDS (chunk c: row c / cpr, k-chunk c % cpr;
   //    the padding chunk and k past kend read 0)
-  constexpr int LR = (MF * 16 + NWAVE - 1) / NWAVE, LV = 8;  // LN: rows per wave, float4 per lane
-  float4 xv[LN ? LR : 1][LN ? LV : 1];
-  if constexpr (LN) {  // rows wave, wave + NWAVE, ... of the fp32 residual stream, whole rows (kper = K)
-    const float* hr = (const float*)a.A;
+  constexpr int LR = (MF * 16 + NWAVE - 1) / NWAVE, LV = LN ? LNV : 1;  // LN: rows per wave, float4 per lane
+  float4 xv[LN ? LR : 1][LV];
+  if constexpr (LN) {
+    // rows wave, wave + NWAVE, ... of the fp32 residual stream, whole rows (kper = K); the
+    // registers of rows past a.rows are neither loaded nor read (every test below is uniform)
+    const float* hr = (const float*)a.A + 4 * lane;
 #pragma unroll
     for (int r = 0; r < LR; ++r) {
       const int row = wave + r * NWAVE;
+      if (row < a.rows) {
 #pragma unroll
-      for (int i = 0; i < LV; ++i) {
-        const int c = 4 * lane + 256 * i;
-        xv[r][i] = (row < a.rows && c < a.K) ? *(const float4*)(hr + (long)row * a.lda + c)
-                                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int i = 0; i < LV; ++i) xv[r][i] = *(const float4*)(hr + (long)row * a.lda + 256 * i);
       }
     }
   } else {
@@ -1044,41 +1045,55 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
       wv[i][c] = buf_load16(rw_rsrc, (s0 + i < s1 && k < kend && woff[c] != OOB) ? woff[c] + k * 2 : OOB);
   }
   if constexpr (LN) {
-    // 1'. each row: mean and variance over its K values (the arithmetic of the residual
-    //     LayerNorm kernel, in the same order), normalised, modulated, bf16 into LDS
+    // nothing below may be scheduled above the weight loads (the row sums would wait for them)
+    __builtin_amdgcn_sched_barrier(0);
+    // 1'. each row: the mean, then the mean squared deviation from it, over its K values (two
+    //     passes; the reductions of the wave's rows interleaved), normalised, modulated, bf16
+    //     into LDS
+    const float inv_k = 1.0f / (float)a.K;
+    float mean[LR], s2[LR];
+#pragma unroll
+    for (int r = 0; r < LR; ++r) {
+      mean[r] = 0.0f;
+      if (wave + r * NWAVE < a.rows) {
+#pragma unroll
+        for (int i = 0; i < LV; ++i) mean[r] += (xv[r][i].x + xv[r][i].y) + (xv[r][i].z + xv[r][i].w);
+      }
+    }
+    wave_sum_n(mean);
+#pragma unroll
+    for (int r = 0; r < LR; ++r) {
+      mean[r] *= inv_k;
+      s2[r] = 0.0f;
+      if (wave + r * NWAVE < a.rows) {
+#pragma unroll
+        for (int i = 0; i < LV; ++i) {
+          const float d0 = xv[r][i].x - mean[r], d1 = xv[r][i].y - mean[r], d2 = xv[r][i].z - mean[r],
+                      d3 = xv[r][i].w - mean[r];
+          s2[r] += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+        }
+      }
+    }
+    wave_sum_n(s2);
 #pragma unroll
     for (int r = 0; r < LR; ++r) {
       const int row = wave + r * NWAVE;
       if (row >= a.rows) break;
-      float sm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < LV; ++i) sm += (xv[r][i].x + xv[r][i].y) + (xv[r][i].z + xv[r][i].w);
-      const float mean = wave_sum(sm) / (float)a.K;
-      float s2 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < LV; ++i) {
-        if (4 * lane + 256 * i < a.K) {
-          const float d0 = xv[r][i].x - mean, d1 = xv[r][i].y - mean, d2 = xv[r][i].z - mean, d3 = xv[r][i].w - mean;
-          s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
-        }
-      }
-      const float rstd = 1.0f / sqrtf(wave_sum(s2) / (float)a.K + 1e-5f);
+      const float rstd = rsqrtf(s2[r] * inv_k + 1e-5f);
 #pragma unroll
       for (int i = 0; i < LV; ++i) {
         const int c = 4 * lane + 256 * i;
-        if (c < a.K) {
-          float o[4] = {(xv[r][i].x - mean) * rstd, (xv[r][i].y - mean) * rstd, (xv[r][i].z - mean) * rstd,
-                        (xv[r][i].w - mean) * rstd};
-          if (a.ln_ada) {
-            const float4 sc = *(const float4*)(a.ln_ada + c);
-            const float4 sh = *(const float4*)(a.ln_ada + a.K + c);
-            o[0] = o[0] * (1.0f + sc.x) + sh.x;
-            o[1] = o[1] * (1.0f + sc.y) + sh.y;
-            o[2] = o[2] * (1.0f + sc.z) + sh.z;
-            o[3] = o[3] * (1.0f + sc.w) + sh.w;
-          }
-          *(uint2*)&skl[row * rs + c] = make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
+        float o[4] = {(xv[r][i].x - mean[r]) * rstd, (xv[r][i].y - mean[r]) * rstd, (xv[r][i].z - mean[r]) * rstd,
+                      (xv[r][i].w - mean[r]) * rstd};
+        if (a.ln_ada) {
+          const float4 sc = *(const float4*)(a.ln_ada + c);
+          const float4 sh = *(const float4*)(a.ln_ada + a.K + c);
+          o[0] = o[0] * (1.0f + sc.x) + sh.x;
+          o[1] = o[1] * (1.0f + sc.y) + sh.y;
+          o[2] = o[2] * (1.0f + sc.z) + sh.z;
+          o[3] = o[3] * (1.0f + sc.w) + sh.w;
         }
+        *(uint2*)&skl[row * rs + c] = make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
       }
     }
     __syncthreads();  // 3. the staged rows are complete (weight loads may still be in flight)
@@ -1137,11 +1152,11 @@ static size_t skinny_lds_bytes(const GemmArgs& a, int mf, int nc, int nwave) {
   return bytes <= SKL_MAX_LDS ? (size_t)bytes : 0;
 }
 
-template <int MF, int NC, int NWAVE, bool LN = false>
+template <int MF, int NC, int NWAVE>
 static hipError_t skinny_lds_kind(const GemmArgs& a, const Epi& e, int splits, size_t lds, hipStream_t s) {
   dim3 grid((a.N + 16 * NC - 1) / (16 * NC), a.groups, splits), blk(64 * NWAVE);
 #define GR00T_SKL_CASE(K) \
-  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K, LN>), grid, blk, lds, s, a, e); break;
+  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K>), grid, blk, lds, s, a, e); break;
   switch (e.kind) {
     GR00T_SKL_CASE(EPI_STORE)
     GR00T_SKL_CASE(EPI_RESID_ADD)
@@ -1151,6 +1166,22 @@ static hipError_t skinny_lds_kind(const GemmArgs& a, const Epi& e, int splits, s
     default: return hipErrorInvalidValue;
   }
 #undef GR00T_SKL_CASE
+  return hipGetLastError();
+}
+
+// LayerNorm folded in (the MLP-up projection at a few rows): plain stores only, K = 256 LNV.
+template <int MF>
+static hipError_t skinny_ln_kind(const GemmArgs& a, const Epi& e, size_t lds, hipStream_t s) {
+  dim3 grid((a.N + 31) / 32, 1, 1), blk(512);
+  if (e.kind != EPI_STORE) return hipErrorInvalidValue;
+  switch (a.K / 256) {
+    case 4: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, 2, 8, EPI_STORE, 4>), grid, blk, lds, s, a, e); break;
+    case 5: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, 2, 8, EPI_STORE, 5>), grid, blk, lds, s, a, e); break;
+    case 6: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, 2, 8, EPI_STORE, 6>), grid, blk, lds, s, a, e); break;
+    case 7: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, 2, 8, EPI_STORE, 7>), grid, blk, lds, s, a, e); break;
+    case 8: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, 2, 8, EPI_STORE, 8>), grid, blk, lds, s, a, e); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1317,7 +1348,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a_in, const Epi& e, DType wt, hipStr
     // 32 columns per workgroup: the rows held in registers allow one workgroup per CU, so
     // half as many workgroups fit the chip in one round
     const size_t lds = skinny_lds_bytes(a, a.rows <= 16 ? 1 : 2, 2, 8);
-    return a.rows <= 16 ? skinny_lds_kind<1, 2, 8, true>(a, e, 1, lds, s) : skinny_lds_kind<2, 2, 8, true>(a, e, 1, lds, s);
+    return a.rows <= 16 ? skinny_ln_kind<1>(a, e, lds, s) : skinny_ln_kind<2>(a, e, lds, s);
   }
   if (a.chunks) {
     // category buckets: 128-row tiles, one chunk of at most chunk_cap samples of `rows` rows

@@ -59,15 +59,99 @@ __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void st<bf16>(bf16* p, float v) { p->u = f_to_bf16(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Wave64 reductions in the pairing of the xor butterfly: lane i combines its value with
+// that of lane i ^ 32, then i ^ 16, i ^ 8, i ^ 4, i ^ 2, i ^ 1. The stages run on the SIMD
+// rather than through LDS: i ^ 32 and i ^ 16 with the gfx950 permlane swaps (a swap of a
+// register with itself leaves, in every lane, the lane's own value in one result and its
+// partner's in the other), i ^ 8 and i ^ 4 as rotations of each 16-lane row by 8 and by 4
+// (once the values repeat with period 16, resp. 8, inside a row, the rotated-in value is the
+// xor partner's), i ^ 2 and i ^ 1 as quad permutations. Every stage combines the same two
+// operands as the butterfly, so the result is bitwise that of the butterfly, in every lane.
+// All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {  // row_mask, bank_mask 0xF: every lane
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_ROW_ROR8 = 0x128, DPP_ROW_ROR4 = 0x124, DPP_QUAD_XOR2 = 0x4E, DPP_QUAD_XOR1 = 0xB1;
+
+// own and partner value (in either order) for partner lane i ^ 32 (L32) or i ^ 16
+template <bool L32>
+__device__ __forceinline__ void xor_pair(float v, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (L32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+  }
+}
+
+struct SumOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// stages i ^ 32 and i ^ 16 of N independent values, interleaved
+template <int N, typename Op>
+__device__ __forceinline__ void wave_reduce_rows(float (&v)[N], Op op) {
+  float a[N], b[N];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  for (int j = 0; j < N; ++j) xor_pair<true>(v[j], a[j], b[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(a[j], b[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) xor_pair<false>(v[j], a[j], b[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(a[j], b[j]);
+}
+// stages i ^ 8 .. i ^ 1 (inside 16-lane rows) of N independent values, interleaved
+template <int N, typename Op>
+__device__ __forceinline__ void wave_reduce_in_row(float (&v)[N], Op op) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(v[j], dpp_f<DPP_ROW_ROR8>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(v[j], dpp_f<DPP_ROW_ROR4>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(v[j], dpp_f<DPP_QUAD_XOR2>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = op(v[j], dpp_f<DPP_QUAD_XOR1>(v[j]));
+}
+// N independent wave sums (each bitwise the butterfly's), interleaved
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+  wave_reduce_rows(v, SumOp{});
+  wave_reduce_in_row(v, SumOp{});
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  float a[1] = {v};
+  wave_sum_n(a);
+  return a[0];
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  float a[1] = {v};
+  wave_reduce_rows(a, MaxOp{});
+  wave_reduce_in_row(a, MaxOp{});
+  return a[0];
+}
+// the stages i ^ 16 then i ^ 32 alone (values that already agree inside each 16-lane row)
+template <typename Op>
+__device__ __forceinline__ float across_rows_16_32(float v, Op op) {
+  float a, b;
+  xor_pair<false>(v, a, b);
+  v = op(a, b);
+  xor_pair<true>(v, a, b);
+  return op(a, b);
+}
+// sum over the 16-lane row (partners i ^ 8 .. i ^ 1), bitwise the butterfly's
+__device__ __forceinline__ float row16_sum(float v) {
+  float a[1] = {v};
+  wave_reduce_in_row(a, SumOp{});
+  return a[0];
 }
 
 // erf from Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26

@@ -484,8 +484,7 @@ __device__ __forceinline__ void attn_tile(const bf16x8_v (&qfr)[QF][(HD + 31) / 
 #pragma unroll
       for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, ((mybits >> i) & 1u) ? sc[i >> 2][i & 3] : -INFINITY);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = across_rows_16_32(tmax, MaxOp{});
     const float mnew = fmaxf(m[qf], tmax * sl2);
     const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qf] - mnew);
     float p[8];
@@ -498,8 +497,7 @@ __device__ __forceinline__ void attn_tile(const bf16x8_v (&qfr)[QF][(HD + 31) / 
         p[i] = ((mybits >> i) & 1u) ? __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mnew)) : 0.0f;
     }
     float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = across_rows_16_32(psum, SumOp{});
     l[qf] = l[qf] * alpha + psum;
     m[qf] = mnew;
     const bf16x8_v pf = __builtin_bit_cast(

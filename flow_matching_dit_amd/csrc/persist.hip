@@ -306,13 +306,11 @@ __device__ void ln_rows(const float* hx, const float2* stat /* [NWG][SMAX] of th
   }
   if (t < 16 * S) {
     float sm = p0.x + p1.x;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) sm += __shfl_xor(sm, o, 16);
+    sm = row16_sum(sm);
     const float mean = sm / (float)NWG;
     const float d0 = p0.x - mean, d1 = p1.x - mean;
     float M = (p0.y + p1.y) + (float)CW * (d0 * d0 + d1 * d1);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) M += __shfl_xor(M, o, 16);
+    M = row16_sum(M);
     if ((t & 15) == 0) rs[srow] = make_float2(mean, 1.0f / sqrtf(M / (float)PD + 1e-5f));
   }
   __syncthreads();
@@ -539,13 +537,11 @@ __device__ __forceinline__ void publish_h(float4 hs, bool hown, int hrow, int hc
   if (hown) *(float4*)(hx + hrow * PD + hcol) = hs;
   if (t < 16 * S) {  // whole 16-lane groups: the shuffles below stay within a row
     float sm = hown ? (hs.x + hs.y) + (hs.z + hs.w) : 0.f;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) sm += __shfl_xor(sm, o, 16);
+    sm = row16_sum(sm);
     const float m = sm / (float)CW;
     const float d0 = hs.x - m, d1 = hs.y - m, d2 = hs.z - m, d3 = hs.w - m;
     float q = hown ? (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3) : 0.f;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) q += __shfl_xor(q, o, 16);
+    q = row16_sum(q);
     if ((t & 15) == 0) stat_wg[hrow] = make_float2(m, q);
   }
 }

@@ -972,10 +972,11 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_kernel(GemmArgs a, Epi
 // whole slice of K (at most KC k-steps) are already in flight. LN: the rows are the fp32
 // residual stream instead, normalised (GemmArgs::ln) by the waves as they stage them.
 constexpr int SKL_MAX_LDS = 64 * 1024;
-template <int MF, int NC, int NWAVE, int EK, int LNV = 0>
+template <int MF, int NC, int NWAVE, int EK, int LNV = 0, int KCW = 8>
 __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a, Epi e) {
-  constexpr int KC = 8;
   constexpr bool LN = LNV > 0;  // LN: the rows are K = 256 LNV fp32 values, normalised here
+  // k-steps of 32 loaded per wave (at most): with the LayerNorm, 8 waves over K = 256 LNV
+  constexpr int KC = LN ? LNV : KCW;
   extern __shared__ __attribute__((aligned(1024))) uint16_t skl[];
   const int g = blockIdx.y;
   const int split = blockIdx.z;
@@ -1036,6 +1037,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
   int woff[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) woff[c] = (n0 + c * 16 + lr < a.N) ? (n0 + c * 16 + lr) * a.K * 2 : OOB;
+  // (unconditional, so that the compiler's waits before the products stay per load; a load
+  // at an out-of-range offset still takes its turn on the CU's load path, so the launcher
+  // picks KC = the k-steps per wave where it can)
   uint4 wv[KC][NC];
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
@@ -1152,11 +1156,11 @@ static size_t skinny_lds_bytes(const GemmArgs& a, int mf, int nc, int nwave) {
   return bytes <= SKL_MAX_LDS ? (size_t)bytes : 0;
 }
 
-template <int MF, int NC, int NWAVE>
+template <int MF, int NC, int NWAVE, int KC>
 static hipError_t skinny_lds_kind(const GemmArgs& a, const Epi& e, int splits, size_t lds, hipStream_t s) {
   dim3 grid((a.N + 16 * NC - 1) / (16 * NC), a.groups, splits), blk(64 * NWAVE);
 #define GR00T_SKL_CASE(K) \
-  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K>), grid, blk, lds, s, a, e); break;
+  case K: hipLaunchKernelGGL((gemm_skinny_lds_kernel<MF, NC, NWAVE, K, 0, KC>), grid, blk, lds, s, a, e); break;
   switch (e.kind) {
     GR00T_SKL_CASE(EPI_STORE)
     GR00T_SKL_CASE(EPI_RESID_ADD)
@@ -1202,14 +1206,55 @@ static hipError_t skinny_kind(const GemmArgs& a, const Epi& e, int splits, hipSt
   return hipGetLastError();
 }
 
+// Compute units of the current device (one query per process).
+static int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
+// The bf16 skinny kernel with staged rows streams each weight once; what bounds it is the
+// load path of the busiest CU: every workgroup reads its 16 nc weight columns over its split
+// of K and, in addition, the whole activation rows of that split (the same for every
+// workgroup), and a CU holds ceil(workgroups / CUs) of them. Bytes through that CU:
+static long skinny_cu_bytes(int rows, int N, int kper, int groups, int splits, int nc) {
+  const long wgs = (long)((N + 16 * nc - 1) / (16 * nc)) * groups * splits;
+  return ((wgs + device_cus() - 1) / device_cus()) * 2l * kper * (16 * nc + rows);
+}
+// Column fragments per workgroup (1 or 3) for a launch of the staged-rows kernel, 0 if it
+// does not fit: 3 where that moves at least 5% fewer bytes through the busiest CU.
+static int skinny_lds_nc(const GemmArgs& a, int mf, int splits) {
+  const int kper = a.k_per_split;
+  if (kper % 128 != 0 || kper > 2048) return 0;
+  const int nwave1 = kper >= 1024 ? 8 : 4;
+  if (kper > nwave1 * 256 || !skinny_lds_bytes(a, mf, 1, nwave1)) return 0;
+  if (mf <= 2 && skinny_lds_bytes(a, mf, 3, 8) &&
+      skinny_cu_bytes(a.rows, a.N, kper, a.groups, splits, 3) * 20 <
+          skinny_cu_bytes(a.rows, a.N, kper, a.groups, splits, 1) * 19)
+    return 3;
+  return 1;
+}
+
 template <int MF>
 static hipError_t skinny_go(const GemmArgs& a, const Epi& e, bool fp8, int splits, hipStream_t s) {
-  // one chunk of KC = 8 k-steps per wave: 8 waves cover a split of up to 2048, 4 up to 1024
-  const int nwave = a.k_per_split >= 1024 ? 8 : 4;
-  if (!fp8 && a.k_per_split <= nwave * 256 && (a.k_per_split % 128) == 0) {
-    const size_t lds = skinny_lds_bytes(a, MF, 1, nwave);
-    if (lds) return nwave == 8 ? skinny_lds_kind<MF, 1, 8>(a, e, splits, lds, s) : skinny_lds_kind<MF, 1, 4>(a, e, splits, lds, s);
+  // KC k-steps of 32 per wave: 8 waves cover a split of up to 2048, 4 up to 1024; where the
+  // k-steps divide evenly into 3 or 6 per wave of 8, exactly that many (no idle loads)
+  const int nc = fp8 ? 0 : skinny_lds_nc(a, MF, splits);
+  if (nc) {
+    const int nwave = (a.k_per_split >= 1024 || nc > 1) ? 8 : 4;
+    const size_t lds = skinny_lds_bytes(a, MF, nc, nwave);
+    const int nsteps = a.k_per_split / 32;
+    if (nc == 3)
+      return nsteps == 24 ? skinny_lds_kind<MF, 3, 8, 3>(a, e, splits, lds, s) : skinny_lds_kind<MF, 3, 8, 8>(a, e, splits, lds, s);
+    if (nwave == 8)
+      return nsteps == 48 ? skinny_lds_kind<MF, 1, 8, 6>(a, e, splits, lds, s) : skinny_lds_kind<MF, 1, 8, 8>(a, e, splits, lds, s);
+    return skinny_lds_kind<MF, 1, 4, 8>(a, e, splits, lds, s);
   }
+  const int nwave = a.k_per_split >= 1024 ? 8 : 4;
   if (a.k_per_split >= 1024)
     return fp8 ? skinny_kind<MF, 8, true>(a, e, splits, s) : skinny_kind<MF, 8, false>(a, e, splits, s);
   return fp8 ? skinny_kind<MF, 4, true>(a, e, splits, s) : skinny_kind<MF, 4, false>(a, e, splits, s);
@@ -1292,8 +1337,28 @@ static int tile_choice(int rows, int N, int groups) {
 
 // Smallest split count that gives >= 240 workgroups (or leaves <= 512 k per split),
 // else the largest valid one (at most 8, each split a multiple of 64 deep).
-int gemm_mfma_splits(int rows, int N, int K, int groups) {
+int gemm_mfma_splits(int rows, int N, int K, int groups, bool bf16w) {
   static const int bm[6] = {256, 256, 64, 32, 16, 128}, bn[6] = {128, 128, 128, 64, 64, 64};
+  if (rows <= 32 && bf16w) {
+    // staged-rows kernel: the split depth (and column fragments) with the fewest bytes
+    // through the busiest CU; a deeper split must save more than 5% (each split is one more
+    // partial for the next norm to add)
+    GemmArgs a{};
+    a.rows = rows;
+    a.N = N;
+    a.groups = groups;
+    int best = 0;
+    long best_b = 0;
+    for (int s = 1; s <= 8; ++s) {
+      if (K % (128 * s) != 0) continue;
+      a.k_per_split = K / s;
+      const int nc = skinny_lds_nc(a, rows <= 16 ? 1 : 2, s);
+      if (!nc) continue;
+      const long b = skinny_cu_bytes(rows, N, K / s, groups, s, nc);
+      if (!best || b * 20 < best_b * 19) best = s, best_b = b;
+    }
+    if (best) return best;
+  }
   if (rows <= 64) {
     // skinny kernel: 8 waves split K inside a workgroup, each holding one chunk of 8 k-steps
     // (256 deep) in flight; deeper K is split across workgroups

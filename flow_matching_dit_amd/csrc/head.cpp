@@ -633,7 +633,7 @@ hipError_t resid_gemm(gr00t_head* h, const GemmArgs& a, DType at, DType wt, long
   Epi e = ep_store(h->w.h, true, a.N);
   const bool mfma = at == DT_BF16 && (wt == DT_BF16 || wt == DT_FP8) && a.K % 16 == 0 && a.lda % 8 == 0 &&
                     a.N % 4 == 0;
-  const int splits = mfma && !direct ? gemm_mfma_splits(a.rows, a.N, a.K, a.groups) : 1;
+  const int splits = mfma && !direct ? gemm_mfma_splits(a.rows, a.N, a.K, a.groups, wt == DT_BF16) : 1;
   if (splits > 1) {
     e.kind = EPI_PARTIAL;
     e.out = h->w.part;

@@ -99,8 +99,9 @@ hipError_t launch_gemm_a8(const GemmArgs& a, const Epi& e, hipStream_t s);
 // folded LayerNorm (GemmArgs::ln): at most 32 rows, bf16 weights, 1024 <= K <= 2048, K a
 // multiple of 256, and the staged rows within the kernel's LDS budget.
 bool gemm_ln_fits(int rows, int K, DType wt);
-// K splits the MFMA GEMM would use for a split-K launch of this shape (1 = none).
-int gemm_mfma_splits(int rows, int N, int K, int groups);
+// K splits the MFMA GEMM would use for a split-K launch of this shape (1 = none); bf16w:
+// bf16 weights (few rows may then take the staged-rows skinny kernel).
+int gemm_mfma_splits(int rows, int N, int K, int groups, bool bf16w);
 
 // LayerNorm over rows of width D (eps 1e-5, population variance):
 //   y = (x - mean) / sqrt(var + eps) [* gamma + beta] [* (1 + scale) + shift]

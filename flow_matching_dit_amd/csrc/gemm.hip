@@ -1019,6 +1019,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gemm_skinny_lds_kernel(GemmArgs a,
         for (int i = 0; i < LV; ++i) xv[r][i] = *(const float4*)(hr + (long)row * a.lda + 256 * i);
       }
     }
+    // every wave's row loads enter the CU's load queue before any weight load: the rows are
+    // needed first (for the LayerNorm, while the weights stream). No wait for their data.
+    asm volatile("s_barrier" ::: "memory");
   } else {
     for (int j = wave; j * 64 < tc; j += NWAVE) {
       const int c = j * 64 + lane;

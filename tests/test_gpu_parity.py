@@ -132,6 +132,16 @@ def test_folded_layernorm_parity_b1():
     _parity(small("dit32_bf16_b1", hidden=1536, num_heads=32, ff_dim=3072), flags=H.FLAG_USE_GRAPH, prepare=True)
 
 
+@pytest.mark.parametrize("hidden,heads,hz", [(1024, 16, 16), (1280, 20, 16), (1792, 28, 8), (2048, 32, 16)])
+def test_folded_layernorm_widths_parity_b1(hidden, heads, hz):
+    # the folded LayerNorm is compiled per width / 256 (4, 5, 7 and 8 here, 6 above; horizon 8:
+    # 9 rows, one row fragment), and the skinny projections take their split depth, tile width
+    # and k-steps per wave from the shape
+    w = small("dit32_bf16_b1", hidden=hidden, num_heads=heads, head_dim=hidden // heads, ff_dim=2 * hidden)
+    w = replace(w, cfg=replace(w.cfg, action_horizon=hz))
+    _parity(w, flags=H.FLAG_USE_GRAPH, prepare=True)
+
+
 def test_wave_per_head_attention_parity():
     # 64 samples x 16 heads of width 48: at >= 1024 (sample, head) pairs attention runs one
     # wave per pair (ragged VL lengths, skipped key tiles); the oracle runs on sampled rows

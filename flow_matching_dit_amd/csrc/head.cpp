@@ -1149,6 +1149,29 @@ int check_inputs(gr00t_head* h, const gr00t_inputs* in, const void* out, bool re
 }
 
 // Strict-mode id check on the host, and the deferred report of bad ids seen on the device.
+// After a fallback away from a kernel that captured graphs may hold: wait for the device, drop
+// every captured graph and capture the prepared step graphs again (whole-call graphs are
+// captured anew once their buffers repeat).
+int recapture_graphs(gr00t_head* h) {
+  if (h->graphs.empty() && h->call_graphs.empty()) return GR00T_OK;
+  HIPCHK(h, hipDeviceSynchronize());
+  std::vector<std::pair<int, int>> keys;
+  for (auto& kv : h->graphs) {
+    keys.push_back(kv.first);
+    (void)hipGraphExecDestroy(kv.second);
+  }
+  for (auto& kv : h->call_graphs) (void)hipGraphExecDestroy(kv.second);
+  h->graphs.clear();
+  h->call_graphs.clear();
+  h->call_order.clear();
+  h->last_call = CallKey{};
+  for (const auto& k : keys) {
+    const int rc = gr00t_prepare(h, k.first, k.second);
+    if (rc != GR00T_OK) return rc;
+  }
+  return GR00T_OK;
+}
+
 int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
   uint32_t newest = h->bad_reported, perr = h->persist_err_reported;
   int sample = -1;
@@ -1168,7 +1191,9 @@ int pre_call_checks(gr00t_head* h, const gr00t_inputs* in, hipStream_t s) {
   (void)hipGetLastError();  // a not-ready query leaves no error behind
   if (perr != h->persist_err_reported) {
     h->persist_err_reported = perr;
-    h->persist_ok = false;  // later calls take the launch-per-step path
+    h->persist_ok = false;  // later calls take the launch-per-step path, also in the graphs
+    const int rc = recapture_graphs(h);
+    if (rc != GR00T_OK) return rc;
     return fail(h, GR00T_E_DEVICE_ERROR,
                 "an earlier call's persistent block kernel gave up (its workgroups were not all resident at once, or not "
                 "32 on each XCD); its result is invalid, and the handle now launches the blocks step by step");

@@ -269,3 +269,25 @@ def test_create_refuses_oversized_mlp_width():
     cfg = replace(synth.WORKLOADS["dit32_bf16_b64"].cfg, ff_dim=1 << 20)
     with pytest.raises(H.Gr00tError, match="one MLP weight matrix"):
         H.Gr00tHead(cfg, max_batch=1, max_vl_len=8)
+
+
+def test_create_accepts_every_declared_flag_and_refuses_others():
+    """Every GR00T_FLAG_* the header declares is accepted at create (W8A8 with e4m3 weights);
+    a bit it does not declare is refused."""
+    src = open(os.path.join(ROOT, "include", "gr00t_head.h")).read()
+    flags = {m.group(1): int(m.group(2), 16) for m in re.finditer(r"#define GR00T_FLAG_(\w+) (0x[0-9a-fA-F]+)u", src)}
+    assert {"STRICT", "USE_GRAPH", "W8A8", "PERSIST", "NO_BUCKETS"} <= set(flags)
+    lib = H.load_library()
+    for name, bit in flags.items():
+        assert getattr(H, "FLAG_" + name) == bit
+        c = H.make_config(_cfg(precision="fp8a8" if name == "W8A8" else "bf16"), 1, 8, flags=bit)
+        out = ctypes.c_void_p()
+        assert lib.gr00t_create(ctypes.byref(c), 0, ctypes.byref(out)) == 0, (name, lib.gr00t_last_error(None))
+        lib.gr00t_destroy(out)
+    undeclared = 1
+    while undeclared in flags.values():
+        undeclared <<= 1
+    c = H.make_config(_cfg(precision="bf16"), 1, 8, flags=undeclared)
+    out = ctypes.c_void_p()
+    assert lib.gr00t_create(ctypes.byref(c), 0, ctypes.byref(out)) == -1
+    assert b"unknown flag bits" in lib.gr00t_last_error(None)

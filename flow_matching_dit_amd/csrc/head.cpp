@@ -19,6 +19,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <new>
@@ -185,6 +186,9 @@ struct gr00t_head {
   void* persist_base = nullptr;
   PBlock* persist_blocks = nullptr;
   uint32_t persist_err_reported = 0;
+  // polls before one of its waits gives up (0: the kernel's default); GR00T_PERSIST_SPIN at
+  // create, for tests of the fallback
+  unsigned persist_spin = 0;
   // (B, L_pad) of the VL key/value caches and key masks in the workspace: those of the last
   // call that ran the full prologue (0, 0: none yet)
   int kv_B = 0, kv_L = 0;
@@ -1006,6 +1010,7 @@ int run_steps(gr00t_head* h, int B, int L, int k0, int k1, bool euler, hipStream
       pa.code = h->w.code;
       pa.L = L;
       pa.text_every = c.attend_text_every_n_blocks;
+      pa.spin = h->persist_spin;
       LAUNCH(h, s, K_BLOCKS, launch_dit_b1_persist(pa, s));
     }
     for (int l = 0; l < Nl && !use_persist(h, B, L, per_sample); ++l) {
@@ -1298,6 +1303,7 @@ int gr00t_create(const gr00t_config* cfg, int device, gr00t_head** out) {
     return GR00T_E_OOM;
   }
   h->cfg = *cfg;
+  if (const char* sp = std::getenv("GR00T_PERSIST_SPIN")) h->persist_spin = (unsigned)std::strtoul(sp, nullptr, 10);
   h->device = device;
   h->act = cfg->act_dtype == GR00T_F32 ? DT_F32 : DT_BF16;
   build_specs(h);

@@ -223,6 +223,7 @@ struct PersistArgs {
   float2* statx;
   unsigned* ctl;
   unsigned long long* trace;  // phase timestamps (written by GR00T_PHASE_TRACE builds only)
+  unsigned spin;              // polls before a wait gives up (0: 2^20)
 };
 // Words of the phase timestamp area (2 workgroups x 64 blocks x 16 boundaries).
 constexpr int persist_trace_words() { return 2 * 64 * 16; }

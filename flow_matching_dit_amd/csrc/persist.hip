@@ -53,7 +53,7 @@ constexpr int RCH = 17;                         // LayerNorm rows per pass
 constexpr int KQ = 7;                           // k-steps per wave, K = 1536 (48 k-steps of 32)
 constexpr int KD = 4;                           // k-steps per wave, K = 768 (24 k-steps)
 constexpr int WA = 2 * KQ, WBN = 3 * KD;        // weight fragments per lane: q / MLP up, o / MLP down
-constexpr unsigned SPIN = 1u << 20;             // polls before a wait gives up
+constexpr unsigned SPIN = 1u << 20;             // polls before a wait gives up (PersistArgs::spin = 0)
 
 // control words, one 256-byte line each
 enum : int {
@@ -117,8 +117,8 @@ __device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t r, int off, float4
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16);
 }
 
-__device__ bool spin_ge(const unsigned* p, unsigned target, unsigned* ctl) {
-  for (unsigned i = 0; i < SPIN; ++i) {
+__device__ bool spin_ge(const unsigned* p, unsigned target, unsigned* ctl, unsigned spin) {
+  for (unsigned i = 0; i < spin; ++i) {
     if ((int)(ld_ag(p) - target) >= 0) return true;
     if ((i & 31u) == 31u && ld_ag(ctl + C_ABORT)) return false;
   }
@@ -134,7 +134,7 @@ __device__ bool spin_ge(const unsigned* p, unsigned target, unsigned* ctl) {
 // bandwidth has taken it; here that stall overlaps the wait). After an XCD barrier the L1 is
 // invalidated so that the reads that follow see the other workgroups' stores in L2.
 template <bool DEV, typename Pre>
-__device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag, Pre&& pre) {
+__device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag, unsigned spin, Pre&& pre) {
   const int wave = threadIdx.x >> 6;
   vm_wait<0>();
   __syncthreads();
@@ -147,14 +147,14 @@ __device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag, Pre&& pr
       const unsigned old = add_ag(ctl + C_XARR + 64 * x, 1u);
       if (old + 1 == (unsigned)NWG * n) {  // last of the XCD: arrive for the XCD, then release it
         add_ag(ctl + C_DEV, 1u);
-        ok = spin_ge(ctl + C_DEV, (unsigned)NX * n, ctl);
+        ok = spin_ge(ctl + C_DEV, (unsigned)NX * n, ctl, spin);
         if (ok) st_ag(ctl + C_XREL + 64 * x, n);
       } else {
-        ok = spin_ge(ctl + C_XREL + 64 * x, n, ctl);
+        ok = spin_ge(ctl + C_XREL + 64 * x, n, ctl, spin);
       }
     } else {
       add_ag(ctl + C_XBAR + 64 * x, 1u);
-      ok = spin_ge(ctl + C_XBAR + 64 * x, (unsigned)NWG * n, ctl);
+      ok = spin_ge(ctl + C_XBAR + 64 * x, (unsigned)NWG * n, ctl, spin);
     }
     *sflag = ok ? 1 : 0;
   }
@@ -163,8 +163,8 @@ __device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag, Pre&& pr
   return __builtin_amdgcn_readfirstlane(*sflag) != 0;  // uniform: the loop stays scalar
 }
 template <bool DEV>
-__device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag) {
-  return pbarrier<DEV>(ctl, x, n, sflag, [] {});
+__device__ bool pbarrier(unsigned* ctl, int x, unsigned& n, int* sflag, unsigned spin) {
+  return pbarrier<DEV>(ctl, x, n, sflag, spin, [] {});
 }
 
 // ------------------------------------------------------------------ weight fragments
@@ -558,6 +558,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
   const bool cw = wave < NWAVE;       // compute wave (wave NWAVE: no weights; the barriers' polls)
   const int S = a.S;
   unsigned* ctl = a.ctl;
+  const unsigned spin = a.spin ? a.spin : SPIN;
   unsigned nbx = 0, nbd = 0;
   __shared__ int sxl[2];
   if (t == 0) {
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
   uint4 wa[WA], wb[WBN];
   floatx4_t acc[3][2];
   publish_h(hs, (t & 15) < 12 && t / 16 < S, t / 16, CW * li + 4 * (t & 15), t, S, hx, stat_wg);
-  bool ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] {
+  bool ok = pbarrier<false>(ctl, x, nbx, &sflag, spin, [&] {
     const PBlock B0 = uniform_block(a.blocks, 0);
     load_wq<0, KQ>(wa, B0.wq, B0.nq == 3, x, li, wave, lane);
     load_wo(wb, B0.wo, x, li, wave, lane);
@@ -625,13 +626,13 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
       }
     }
     PTS(2);
-    ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w1<0, 3>(wa, B.w1, x, li, wave, lane); });
+    ok = pbarrier<false>(ctl, x, nbx, &sflag, spin, [&] { load_w1<0, 3>(wa, B.w1, x, li, wave, lane); });
     if (!ok) break;
     PTS(3);
     // ---- attention of one head for up to 4 queries
     attention_head(a, self, cross_idx, (l % (2 * a.text_every) == 0) ? 1 : 2, x, li, t, asc);
     PTS(4);
-    ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w1<3, KQ>(wa, B.w1, x, li, wave, lane); });
+    ok = pbarrier<false>(ctl, x, nbx, &sflag, spin, [&] { load_w1<3, KQ>(wa, B.w1, x, li, wave, lane); });
     if (!ok) break;
     PTS(5);
     // ---- o projection: this XCD's partial sum over its 192 attention columns, for the
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
       }
     }
     PTS(6);
-    ok = pbarrier<true>(ctl, x, nbd, &sflag, [&] { load_w2<0, 2>(wb, B.w2, x, li, wave, lane); });
+    ok = pbarrier<true>(ctl, x, nbd, &sflag, spin, [&] { load_w2<0, 2>(wb, B.w2, x, li, wave, lane); });
     if (!ok) break;
     PTS(7);
     // ---- residual: h += sum over the XCDs' partials (fixed order) + bo
@@ -681,7 +682,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
     publish_h(hs, hown, hrow, hcol, t, S, hx, stat_wg);
     par ^= 1;
     PTS(8);
-    ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] { load_w2<2, KD>(wb, B.w2, x, li, wave, lane); });
+    ok = pbarrier<false>(ctl, x, nbx, &sflag, spin, [&] { load_w2<2, KD>(wb, B.w2, x, li, wave, lane); });
     if (!ok) break;
     PTS(9);
     // ---- LayerNorm, MLP up + GELU for the workgroup's 24 MLP columns
@@ -703,7 +704,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
       }
     }
     PTS(11);
-    ok = pbarrier<false>(ctl, x, nbx, &sflag, [&] {
+    ok = pbarrier<false>(ctl, x, nbx, &sflag, spin, [&] {
       if (more) load_wq<0, 3>(wa, uniform(a.blocks[l + 1].wq), a.blocks[l + 1].nq == 3, x, li, wave, lane);
     });
     if (!ok) break;
@@ -737,7 +738,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
       }
     }
     PTS(13);
-    ok = pbarrier<true>(ctl, x, nbd, &sflag, [&] {
+    ok = pbarrier<true>(ctl, x, nbd, &sflag, spin, [&] {
       if (more) {
         const PBlock Bn = uniform_block(a.blocks, l + 1);
         load_wq<3, KQ>(wa, Bn.wq, Bn.nq == 3, x, li, wave, lane);
@@ -765,7 +766,7 @@ __global__ __launch_bounds__(NT) void dit_b1_persist_kernel(PersistArgs a) {
     if (more) publish_h(hs, hown, hrow, hcol, t, S, hx, stat_wg);
     par ^= 1;
     if (!self) ++cross_idx;
-    if (more) ok = pbarrier<false>(ctl, x, nbx, &sflag);
+    if (more) ok = pbarrier<false>(ctl, x, nbx, &sflag, spin);
     PTS(15);
   }
   // the residual stream after the last block (every workgroup holds its 48 columns)

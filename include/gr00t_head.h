@@ -88,7 +88,11 @@ typedef enum gr00t_dtype {
                                    all 256 compute units to itself: a wait that does not end
                                    within its bound gives up, the call's result is then wrong,
                                    the next call reports GR00T_E_DEVICE and the handle falls back
-                                   to the launch-per-step path. Ignored where it does not apply. */
+                                   to the launch-per-step path (its captured graphs are captured
+                                   again). Ignored where it does not apply. The environment
+                                   variable GR00T_PERSIST_SPIN, read at gr00t_create, sets how
+                                   many polls a wait makes before it gives up (tests of the
+                                   fallback; default 2^20). */
 
 #define GR00T_FLAG_NO_BUCKETS 0x10u /* batches of 128 samples or more normally run the
                                        per-embodiment bf16 linears over category buckets (the

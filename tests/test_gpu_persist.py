@@ -77,3 +77,30 @@ def test_persistent_blocks_repeat_bitwise():
     assert np.array_equal(ya, yb)
     for y in yg:
         assert np.array_equal(y, ya)
+
+
+def test_persistent_timeout_falls_back_to_launch_path(monkeypatch):
+    """Failure handling, forced from the host: with a poll budget of one (GR00T_PERSIST_SPIN=1 at
+    create) the persistent kernel's waits give up at once and every workgroup leaves its loop,
+    so the call's result is invalid. The next call reports E_DEVICE_ERROR; from then on the
+    handle runs the blocks launch by launch, also from the graphs it had captured with the
+    persistent kernel (they are captured again), bitwise as a handle without the flag."""
+    w = _b1(2, 16, 300, 256)
+    wt, inp, nz = synth.make_weights(w), synth.make_inputs(w), synth.make_noise(w)
+    say(f"[persist] {w.name}: forced timeout, fallback")
+    ref_h = build_head(w, wt, flags=H.FLAG_USE_GRAPH)
+    y_ref = gpu_action(ref_h, inp, nz, prepare=True)
+    ref_h.close()
+    monkeypatch.setenv("GR00T_PERSIST_SPIN", "1")
+    h = build_head(w, wt, flags=H.FLAG_USE_GRAPH | H.FLAG_PERSIST)
+    monkeypatch.delenv("GR00T_PERSIST_SPIN")
+    gpu_action(h, inp, nz, prepare=True)  # its waits give up: an invalid result, reported next
+    with pytest.raises(H.Gr00tError) as e:
+        gpu_action(h, inp, nz)
+    assert e.value.status == "E_DEVICE_ERROR" and "persistent" in str(e.value)
+    y = gpu_action(h, inp, nz)  # the recaptured step graph: launch by launch
+    assert not _ran_persistent(h, inp, nz)
+    y_again = gpu_action(h, inp, nz)
+    h.close()
+    assert np.array_equal(y, y_ref)
+    assert np.array_equal(y_again, y_ref)
